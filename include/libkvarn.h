@@ -1,0 +1,141 @@
+/* libkvarn -- variance-normalised KV-cache quantisation (KVarN) for AMD MI355X (gfx950).
+ *
+ * Pages cited below (titles abbreviated):
+ *   [HYPHO] blog.hypho.cn, "KV-cache 量化终于能跑生产了？KVarN 用方差归一化打破 vLLM 的吞吐量魔咒"
+ *   [LEHUY] lehuy.net, "KVarN: Backend lượng tử hóa KV-cache gốc của Huawei giúp vLLM ..."
+ *   [OPENAIHUB] openai-hub.net/news/593, "Huawei Cloud open-sources KVarN ..."
+ *
+ * The method (four stages per fixed token tile, [HYPHO] section "它怎么做到的：四步流水线",
+ * [LEHUY] section "Cơ chế hoạt động: Chuẩn hóa phương sai"):
+ *   1. take a raw fp16 K or V tile of 128 tokens x 128 channels,
+ *   2. rotate every token along channels with the orthonormal Hadamard matrix Hn = H_128/sqrt(128),
+ *   3. balance row (token) and column (channel) RMS by alternating Sinkhorn-style passes in
+ *      log space (8 iterations, channels first),
+ *   4. quantise each token's 128 channels with asymmetric round-to-nearest at b bits
+ *      (keys 4 bits, values 2 bits by default: "kvarn_k4v2_g128"), keeping the scales so that
+ *      they can be folded back in when attention reads the cache.
+ * The page size equals the tile size and must be 128 ([HYPHO] section "需要关注的几个问题", item 3).
+ *
+ * Conventions for every call:
+ *   - Ownership: the caller owns and allocates every buffer (cache pool, tails, page table,
+ *     lengths, workspace, outputs).  The library allocates nothing and keeps no per-call state;
+ *     calls on different streams are independent.
+ *   - Pointers marked (device) are device addresses; the call only enqueues work on `stream`
+ *     and returns at once.  The host never reads device memory.
+ *   - Errors detectable on the host (null pointer, unsupported format, bad sizes, workspace too
+ *     small) return a status and launch nothing.  A failed launch returns KVARN_E_HIP.
+ *     Device-side preconditions (valid page ids, pages allocated before a tile fills) are
+ *     documented, not checked.
+ *
+ * Record layout (one record per (page, kv head), this library's own format; the pages fix
+ * none of it).  T = 128 tokens, D = 128 channels, kb / vb = key / value bits:
+ *   [0, 16*T*kb)            K codes, token-major.  Token t owns 16*kb bytes at t*16*kb.  Unit u
+ *                           (0..15) of kb bytes at u*kb holds the codes of channels u + 16*e,
+ *                           e = 0..7, code e at bit kb*e of the little-endian unit.
+ *   [16*T*kb, +16*T*vb)     V codes.  Unit size U = 2*vb bytes (16 codes).  Unit
+ *                           (nb, gr, nl, half) at ((nb*4 + gr)*16 + nl)*2*U + half*U holds channel
+ *                           j = 16*nb + nl for tokens t = 64*half + 16*mb + 4*gr + i (mb, i = 0..3),
+ *                           the code of (mb, i) at bit vb*(4*mb + i).
+ *   then six float32[128]:  c_K, s'_K, m'_K, c_V, s'_V, m'_V.
+ * For a token t of one half, with Y = X Hn, log-scales (u, v) from step 3 and the group
+ * statistics mn_t, s_t of Z = Y exp(-u_t - v_j):  c_j = exp(v_j),  s'_t = exp(u_t) s_t,
+ * m'_t = exp(u_t) mn_t, and the value read back is  xhat_t = Hn (c ⊙ (m'_t + s'_t q_t)).
+ * Record size: 15360 bytes for k4v2, 35840 for k8v8 (vs 65536 for fp16 K+V: 4.27x capacity).
+ */
+#ifndef LIBKVARN_H_
+#define LIBKVARN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVARN_OK = 0,
+  KVARN_E_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes */
+  KVARN_E_UNSUPPORTED = 2, /* a format, block size, head size or GQA ratio this build does not run */
+  KVARN_E_HIP = 3          /* a HIP launch or runtime call failed */
+} kvarn_status;
+
+/* kv-cache dtype string "kvarn_k{K}v{V}_g{G}" ([HYPHO] section "工程实践：一行配置启用";
+ * [LEHUY] section "Dễ dàng tích hợp và sử dụng").  head_dim and block_size are 128; sinkhorn_iters
+ * is 8 (one iteration = one channel pass + one token pass). */
+typedef struct {
+  int32_t k_bits, v_bits, group, head_dim, block_size, sinkhorn_iters;
+} kvarn_format;
+
+/* Parse a dtype string.  "kvarn_k4v2_g128" -> {4, 2, 128, 128, 128, 8}.  Bits must be 2, 4 or 8;
+ * any group other than 128 returns KVARN_E_UNSUPPORTED; malformed strings KVARN_E_INVALID_ARG. */
+kvarn_status kvarn_format_parse(const char* name, kvarn_format* out);
+
+/* Check a format struct filled by hand: same rules as kvarn_format_parse, plus head_dim and
+ * block_size 128 and 0 <= sinkhorn_iters <= 64. */
+kvarn_status kvarn_format_check(const kvarn_format* f);
+
+/* Bytes of one record (one page of one kv head); 0 if the format is invalid. */
+size_t kvarn_record_bytes(const kvarn_format* f);
+
+/* Workspace bytes kvarn_decode_attention needs for these sizes (split-K partial results:
+ * per (sequence, query head, split) a running max, a running sum and 128 accumulators). */
+size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t max_pages_per_seq);
+
+/* Bulk tile quantisation (prefill): stages 1-4 on num_tiles x num_kv_heads tiles.
+ *   k, v       (device) fp16 [num_tiles][128 tokens][num_kv_heads][head_dim]
+ *   dst_pages  (device) int32 [num_tiles]: physical page of each tile
+ *   cache      (device) pool; tile i of head h is written at
+ *              cache + dst_pages[i]*page_stride_bytes + h*kvarn_record_bytes(f)
+ *   page_stride_bytes >= num_kv_heads*record_bytes and a multiple of 16.
+ * Each tile's record depends only on that tile's K and V (no calibration, [HYPHO] section
+ * "KVarN 是什么"). */
+kvarn_status kvarn_quantize_tiles(const kvarn_format* f, int32_t num_tiles, int32_t num_kv_heads,
+                                  const void* k, const void* v, const int32_t* dst_pages, void* cache,
+                                  int64_t page_stride_bytes, hipStream_t stream);
+
+/* Append one token per sequence (decode step).  With len = seq_lens[s] before the call:
+ * tail_k/v[s][h][len % 128] <- k_new/v_new[s][h] (raw fp16); if (len + 1) % 128 == 0 the whole
+ * tail tile of every head is quantised into page page_table[s*max_pages_per_seq + len/128];
+ * finally seq_lens[s] = len + 1.
+ *   k_new, v_new  (device) fp16 [num_seqs][num_kv_heads][head_dim]
+ *   seq_lens      (device) int32 [num_seqs], read then incremented
+ *   tail_k/tail_v (device) fp16 [num_seqs][num_kv_heads][128][head_dim]
+ *   page_table    (device) int32 [num_seqs][max_pages_per_seq]
+ * The page for a filling tile must be allocated in page_table before the call. */
+kvarn_status kvarn_append_token(const kvarn_format* f, int32_t num_seqs, int32_t num_kv_heads,
+                                const void* k_new, const void* v_new, int32_t* seq_lens, void* tail_k,
+                                void* tail_v, const int32_t* page_table, int32_t max_pages_per_seq,
+                                void* cache, int64_t page_stride_bytes, hipStream_t stream);
+
+/* Decode attention over the quantised cache (every step reads all cached tokens, [HYPHO] section
+ * "论文的核心发现：推理场景的误差累积"), with the scales folded in on read ([LEHUY] section
+ * "Cơ chế hoạt động", stage 4): channel scales into the rotated query, token scales into the
+ * logits and the softmax weights, the inverse rotation applied once to the output.
+ * For sequence s with L = seq_lens[s] tokens: full pages 0 .. L/128-1 come from the cache, the
+ * L % 128 newest tokens from the fp16 tail.  Query head hq uses kv head hq / (Hq/Hkv).
+ *   out[s][hq] = softmax(sm_scale * q . K^T) V  (fp16; all zeros when L = 0)
+ *   q, out     (device) fp16 [num_seqs][num_q_heads][head_dim]
+ *   page_table (device) int32 [num_seqs][max_pages_per_seq]; seq_lens (device) int32 [num_seqs]
+ *              with seq_lens[s] < 128*(max_pages_per_seq + 1); max_pages_per_seq sizes the
+ *              split-K grid and the workspace
+ *   workspace  (device) >= kvarn_decode_workspace_bytes(...) bytes, 16-byte aligned
+ * Supported query heads per kv head: 8 and 16. */
+kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, const void* q, const void* cache,
+                                    int64_t page_stride_bytes, const int32_t* page_table,
+                                    int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                    const void* tail_k, const void* tail_v,
+                                    float sm_scale, void* out, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Human-readable name of a status. */
+const char* kvarn_status_string(kvarn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKVARN_H_ */

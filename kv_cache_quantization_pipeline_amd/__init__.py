@@ -1,0 +1,193 @@
+"""Python binding of libkvarn (KVarN KV-cache quantisation for MI355X / gfx950).
+
+Argument marshalling only: every step of the method runs in the HIP kernels of
+libkvarn.so, which this module loads with ctypes.  torch supplies device memory
+and the current stream.  If the library has not been built this module raises
+on first use; there is no CPU fallback.
+
+Functions mirror include/libkvarn.h:
+    format_parse, record_bytes, decode_workspace_bytes,
+    quantize_tiles, append_token, decode_attention
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvarn.so")
+
+KVARN_OK, KVARN_E_INVALID_ARG, KVARN_E_UNSUPPORTED, KVARN_E_HIP = 0, 1, 2, 3
+
+# every C-ABI entry point declared in include/libkvarn.h
+EXPORTS = (
+    "kvarn_format_parse",
+    "kvarn_format_check",
+    "kvarn_record_bytes",
+    "kvarn_decode_workspace_bytes",
+    "kvarn_quantize_tiles",
+    "kvarn_append_token",
+    "kvarn_decode_attention",
+    "kvarn_status_string",
+)
+
+
+class KvarnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class Format(ctypes.Structure):
+    """kvarn_format: bits, group and sizes of one kv-cache dtype."""
+    _fields_ = [("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"Format(k{self.k_bits}v{self.v_bits}_g{self.group}, head_dim={self.head_dim}, "
+                f"block={self.block_size}, iters={self.sinkhorn_iters})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libkvarn.so (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libkvarn.so not found at {LIB_PATH}; run __graft_entry__.build() "
+                               "or python kv_cache_quantization_pipeline_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, flt = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        fp = ctypes.POINTER(Format)
+        L.kvarn_format_parse.restype = i32
+        L.kvarn_format_parse.argtypes = [ctypes.c_char_p, fp]
+        L.kvarn_format_check.restype = i32
+        L.kvarn_format_check.argtypes = [fp]
+        L.kvarn_record_bytes.restype = sz
+        L.kvarn_record_bytes.argtypes = [fp]
+        L.kvarn_decode_workspace_bytes.restype = sz
+        L.kvarn_decode_workspace_bytes.argtypes = [fp, i32, i32, i32, i32]
+        L.kvarn_quantize_tiles.restype = i32
+        L.kvarn_quantize_tiles.argtypes = [fp, i32, i32, vp, vp, vp, vp, i64, vp]
+        L.kvarn_append_token.restype = i32
+        L.kvarn_append_token.argtypes = [fp, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i64, vp]
+        L.kvarn_decode_attention.restype = i32
+        L.kvarn_decode_attention.argtypes = [fp, i32, i32, i32, vp, vp, i64, vp, i32, vp, vp, vp, flt, vp, vp, sz,
+                                             vp]
+        L.kvarn_status_string.restype = ctypes.c_char_p
+        L.kvarn_status_string.argtypes = [i32]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kvarn_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != KVARN_OK:
+        raise KvarnError(status, what)
+
+
+def format_parse(name: str) -> Format:
+    f = Format()
+    _check(lib().kvarn_format_parse(name.encode(), ctypes.byref(f)), f"kvarn_format_parse({name!r})")
+    return f
+
+
+def record_bytes(fmt: Format) -> int:
+    return int(lib().kvarn_record_bytes(ctypes.byref(fmt)))
+
+
+def decode_workspace_bytes(fmt: Format, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                           max_pages_per_seq: int) -> int:
+    return int(lib().kvarn_decode_workspace_bytes(ctypes.byref(fmt), num_seqs, num_q_heads, num_kv_heads,
+                                                  max_pages_per_seq))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def quantize_tiles(fmt: Format, k, v, dst_pages, cache, page_stride_bytes: int, stream=None):
+    """k, v: fp16 [num_tiles, 128, Hkv, 128]; dst_pages: int32 [num_tiles]; cache: uint8 pool."""
+    import torch
+    _need(k, "k", torch.float16, 4)
+    _need(v, "v", torch.float16, 4)
+    _need(dst_pages, "dst_pages", torch.int32, 1)
+    _need(cache, "cache", torch.uint8)
+    if k.shape != v.shape or k.shape[1] != 128 or k.shape[3] != 128 or dst_pages.shape[0] != k.shape[0]:
+        raise ValueError(f"bad shapes k {tuple(k.shape)} v {tuple(v.shape)} dst_pages {tuple(dst_pages.shape)}")
+    st = lib().kvarn_quantize_tiles(ctypes.byref(fmt), k.shape[0], k.shape[2], _ptr(k), _ptr(v), _ptr(dst_pages),
+                                    _ptr(cache), page_stride_bytes, _stream(stream))
+    _check(st, "kvarn_quantize_tiles")
+
+
+def append_token(fmt: Format, k_new, v_new, seq_lens, tail_k, tail_v, page_table, cache, page_stride_bytes: int,
+                 stream=None):
+    """k_new, v_new: fp16 [B, Hkv, 128]; seq_lens int32 [B] (incremented); tails fp16 [B, Hkv, 128, 128];
+    page_table int32 [B, max_pages]."""
+    import torch
+    _need(k_new, "k_new", torch.float16, 3)
+    _need(v_new, "v_new", torch.float16, 3)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(tail_k, "tail_k", torch.float16, 4)
+    _need(tail_v, "tail_v", torch.float16, 4)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(cache, "cache", torch.uint8)
+    B, hkv = k_new.shape[0], k_new.shape[1]
+    if (v_new.shape != k_new.shape or tuple(tail_k.shape) != (B, hkv, 128, 128) or tail_v.shape != tail_k.shape
+            or seq_lens.shape[0] != B or page_table.shape[0] != B):
+        raise ValueError("inconsistent shapes for append_token")
+    st = lib().kvarn_append_token(ctypes.byref(fmt), B, hkv, _ptr(k_new), _ptr(v_new), _ptr(seq_lens), _ptr(tail_k),
+                                  _ptr(tail_v), _ptr(page_table), page_table.shape[1], _ptr(cache),
+                                  page_stride_bytes, _stream(stream))
+    _check(st, "kvarn_append_token")
+
+
+def decode_attention(fmt: Format, q, cache, page_stride_bytes: int, page_table, seq_lens, tail_k, tail_v,
+                     sm_scale: float, out, workspace, num_kv_heads: int, stream=None):
+    """q, out: fp16 [B, Hq, 128]; page_table int32 [B, max_pages]; seq_lens int32 [B];
+    tails fp16 [B, Hkv, 128, 128]; workspace: device tensor of >= decode_workspace_bytes bytes."""
+    import torch
+    _need(q, "q", torch.float16, 3)
+    _need(out, "out", torch.float16, 3)
+    _need(cache, "cache", torch.uint8)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(tail_k, "tail_k", torch.float16, 4)
+    _need(tail_v, "tail_v", torch.float16, 4)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    B, hq = q.shape[0], q.shape[1]
+    if out.shape != q.shape or seq_lens.shape[0] != B or page_table.shape[0] != B:
+        raise ValueError("inconsistent shapes for decode_attention")
+    if tuple(tail_k.shape) != (B, num_kv_heads, 128, 128) or tail_v.shape != tail_k.shape:
+        raise ValueError(f"tails must be [B, Hkv, 128, 128], got {tuple(tail_k.shape)}")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().kvarn_decode_attention(ctypes.byref(fmt), B, hq, num_kv_heads, _ptr(q), _ptr(cache),
+                                      page_stride_bytes, _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+                                      _ptr(tail_k), _ptr(tail_v), float(sm_scale), _ptr(out), _ptr(workspace),
+                                      ws_bytes, _stream(stream))
+    _check(st, "kvarn_decode_attention")

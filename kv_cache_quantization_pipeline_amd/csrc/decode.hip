@@ -1,0 +1,629 @@
+// KVarN decode attention over the packed cache, for gfx950.
+//
+// Scales are folded in on read ([LEHUY] section "Cơ chế hoạt động", stage 4;
+// [HYPHO] section "它怎么做到的：四步流水线", step 4).  With the record of one
+// page, xhat_t = Hn (c ⊙ (m'_t + s'_t q_t)) and Hn symmetric:
+//   q . khat_t = s'_t (q'' . q_t) + m'_t sigma,   q' = Hn q, q'' = c_K ⊙ q', sigma = sum_j q''_j
+//   sum_t p_t vhat_t = Hn ( c_V ⊙ ( sum_t (p_t s'_t) q_t + sum_t p_t m'_t ) )
+// so channel scales go into the rotated query, token scales into the logits and
+// the softmax weights, and Hn is applied once, to the merged output (combine
+// kernel).  Logits are kept in the log2 domain (q' is pre-scaled by
+// sm_scale * log2 e) so the softmax uses exp2.
+//
+// Work split: grid (sequence * kv head, split), 4 waves per workgroup, each wave
+// a run of page groups.  A group is P = 16/G pages (G query heads per kv head)
+// so that the 16 MFMA columns are all used: for QK the A operand is the codes
+// of token rows (16 per M block), K runs over (page, channel) and the B
+// operand is block-diagonal (lane column n = (page e, head g) holds q''_e,g for
+// page e's k-steps, zero elsewhere); for PV the A operand is the weights
+// (row (e, g), K over (page, token)), the B operand the V codes.  Codes become
+// exact fp16 integers in registers (4-bit / 2-bit: bytes read as fp8 e4m3 and
+// scaled by 2^9; 8-bit: 0x6400 | byte minus 1024).  Each wave keeps one
+// running (max, sum, acc) per MFMA row, i.e. per (page parity, head); the
+// workgroup merges its 4 waves x P streams in LDS and writes one split-K
+// partial per query head.
+//
+// The fp16 tail (the len % 128 newest tokens) and the final inverse rotation
+// are handled by the combine kernel.
+
+#include "kvarn_device.h"
+#include "kvarn_internal.h"
+
+namespace kvarn {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <bool HI>
+__device__ __forceinline__ f16x2 fp8b_to_f16(uint32_t w) {
+  // bytes (0,1) or (2,3) of w, each a code 0..15, read as OCP e4m3 (value code * 2^-9) times 2^9
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 512.0f, HI);
+}
+__device__ __forceinline__ f16x2 u8pair_to_f16(uint32_t w) {
+  // (w & 0x00ff00ff) are two bytes in 16-bit lanes: 0x6400 | b is the fp16 value 1024 + b
+  const uint32_t x = (w & 0x00ff00ffu) | 0x64006400u;
+  return __builtin_bit_cast(f16x2, x) - f16x2{static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+}
+__device__ __forceinline__ f16x8 cat4(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// ---- K codes: token 16*mb + nl, units 4*gr .. 4*gr+3 -------------------------
+template <int KB>
+struct KRegs;
+template <>
+struct KRegs<4> {
+  u32x4 w;
+};
+template <>
+struct KRegs<8> {
+  u32x4 w[2];
+};
+
+template <int KB>
+__device__ __forceinline__ void load_k(KRegs<KB>& r, const uint8_t* p) {
+  if constexpr (KB == 4) {
+    r.w = *reinterpret_cast<const u32x4*>(p);
+  } else {
+    r.w[0] = *reinterpret_cast<const u32x4*>(p);
+    r.w[1] = *reinterpret_cast<const u32x4*>(p + 16);
+  }
+}
+
+// Slot s of the MFMA operand at k-step kb holds code e = keperm(s) of unit 4*gr + kb,
+// i.e. channel 4*gr + kb + 16*keperm(s).
+template <int KB>
+__host__ __device__ constexpr int keperm(int s) {
+  return KB == 4 ? (s < 4 ? 2 * s : 2 * (s - 4) + 1)  // 0 2 4 6 1 3 5 7
+                 : ((s & 4) | ((s & 1) << 1) | ((s >> 1) & 1));  // 0 2 1 3 4 6 5 7
+}
+
+template <int KB>
+__device__ __forceinline__ f16x8 dequant_k(const KRegs<KB>& r, int kb) {
+  if constexpr (KB == 4) {
+    const uint32_t w = r.w[kb];
+    const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+    return cat4(fp8b_to_f16<false>(lo), fp8b_to_f16<true>(lo), fp8b_to_f16<false>(hi), fp8b_to_f16<true>(hi));
+  } else {
+    const uint32_t d0 = r.w[kb >> 1][2 * (kb & 1)], d1 = r.w[kb >> 1][2 * (kb & 1) + 1];
+    return cat4(u8pair_to_f16(d0), u8pair_to_f16(d0 >> 8), u8pair_to_f16(d1), u8pair_to_f16(d1 >> 8));
+  }
+}
+
+// ---- V codes: channel 16*nb + nl, tokens with (t >> 2) & 3 == gr ------------------
+template <int VB>
+struct VRegs;
+template <>
+struct VRegs<2> {
+  u32x2 w;  // half 0, half 1
+};
+template <>
+struct VRegs<8> {
+  u32x4 w[2];
+};
+
+template <int VB>
+__device__ __forceinline__ void load_v(VRegs<VB>& r, const uint8_t* p) {
+  if constexpr (VB == 2) {
+    r.w = *reinterpret_cast<const u32x2*>(p);
+  } else {
+    r.w[0] = *reinterpret_cast<const u32x4*>(p);
+    r.w[1] = *reinterpret_cast<const u32x4*>(p + 16);
+  }
+}
+
+// k-step kb covers tokens 32*kb + 16*h + 4*gr + i; register r holds slots
+// (2r, 2r+1) = tokens (h = 0, i = r), (h = 1, i = r).
+template <int VB, int WS>
+__device__ __forceinline__ f16x8 dequant_v_ws(const VRegs<VB>& r, int half) {
+  constexpr int ws = WS;
+  const int kb = 2 * half + WS;
+  if constexpr (VB == 2) {
+    const uint32_t d = r.w[half];
+    return cat4(fp8b_to_f16<WS>(d & 0x03030303u), fp8b_to_f16<WS>((d >> 2) & 0x03030303u),
+                fp8b_to_f16<WS>((d >> 4) & 0x03030303u), fp8b_to_f16<WS>((d >> 6) & 0x03030303u));
+  } else {
+    const uint32_t D0 = r.w[kb >> 1][2 * ws], D1 = r.w[kb >> 1][2 * ws + 1];
+    f16x2 o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // bytes D0.q and D1.q into 16-bit lanes 0 and 1
+      const uint32_t sel = static_cast<uint32_t>(q) | 0x0c00u | (static_cast<uint32_t>(4 + q) << 16) | 0x0c000000u;
+      o[q] = u8pair_to_f16(__builtin_amdgcn_perm(D1, D0, sel));
+    }
+    return cat4(o[0], o[1], o[2], o[3]);
+  }
+}
+template <int VB>
+__device__ __forceinline__ f16x8 dequant_v(const VRegs<VB>& r, int kb) {
+  return (kb & 1) ? dequant_v_ws<VB, 1>(r, kb >> 1) : dequant_v_ws<VB, 0>(r, kb >> 1);
+}
+
+template <int KB, int VB, int P>
+struct Pair {
+  KRegs<KB> kq[P][8];
+  VRegs<VB> vq[P][8];
+  float4 sc[3 * P];  // the P pages' six scale arrays, 16 bytes per chunk
+};
+
+template <int KB, int VB, int P>
+__device__ __forceinline__ void load_pair(Pair<KB, VB, P>& d, const uint8_t* const (&rec)[P], int lane) {
+  constexpr int SOFF = scale_offset(KB, VB);
+  const int nl = lane & 15, gr = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) load_k<KB>(d.kq[e][mb], rec[e] + (16 * mb + nl) * 16 * KB + 4 * gr * KB);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      load_v<VB>(d.vq[e][nb], rec[e] + k_code_bytes(KB) + ((nb * 4 + gr) * 16 + nl) * 4 * VB);
+  }
+#pragma unroll
+  for (int k = 0; k < 3 * P; ++k) {
+    const int c = lane + 64 * k;
+    d.sc[k] = *reinterpret_cast<const float4*>(rec[c / 192] + SOFF + (c % 192) * 16);
+  }
+}
+
+__device__ __forceinline__ f16x8 zero8() {
+  return f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+
+}  // namespace
+
+template <int KB, int VB, int G>
+__global__ __launch_bounds__(256, 1) void decode_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ cache,
+                                                        int64_t page_stride, const int32_t* __restrict__ page_table,
+                                                        int max_pages, const int32_t* __restrict__ seq_lens,
+                                                        int num_q_heads, int num_kv_heads, float qscale,
+                                                        float* __restrict__ ws, int n_splits, int groups_per_split) {
+  constexpr int P = 16 / G;
+  constexpr int R = record_bytes(KB, VB);
+  constexpr int SC = 6 * kCh;   // floats of scales per page
+  constexpr int MRG = 130;      // floats per merged row
+
+  __shared__ float qrot[G][kCh];
+  // per wave: staged scales of the current group (P pages); reused for the merge
+  constexpr int STAGE_FLOATS = 4 * P * SC;
+  constexpr int MERGE_FLOATS = 4 * 16 * MRG;
+  __shared__ float lds[STAGE_FLOATS > MERGE_FLOATS ? STAGE_FLOATS : MERGE_FLOATS];
+
+  const int sh = blockIdx.x;
+  const int s = sh / num_kv_heads;
+  const int h = sh - s * num_kv_heads;
+  const int sp = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, gr = lane >> 4;
+
+  const int len = seq_lens[s];
+  const int n_pages = len >> 7;
+  const int n_groups = (n_pages + P - 1) / P;
+
+  // ---- q' = Hn q * sm_scale * log2(e): 32 threads per head, 4 channels each --------------
+  for (int base = 0; base < G * 32; base += 256) {
+    const int idx = base + tid;
+    if (idx < G * 32) {
+      const int g = idx >> 5, r = idx & 31;
+      const _Float16* qp = q + (static_cast<int64_t>(s) * num_q_heads + h * G + g) * kCh + 4 * r;
+      float x0 = qp[0], x1 = qp[1], x2 = qp[2], x3 = qp[3];
+      float a0 = x0 + x1, a1 = x0 - x1, a2 = x2 + x3, a3 = x2 - x3;
+      float v[4] = {a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+#pragma unroll
+      for (int b = 0; b < 5; ++b) {
+        const bool upper = (r >> b) & 1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float o = __shfl_xor(v[c], 1 << b, 32);
+          v[c] = upper ? o - v[c] : v[c] + o;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qrot[g][4 * r + c] = v[c] * qscale;
+    }
+  }
+  __syncthreads();
+
+  // this lane's QK column / PV row n = nl: page e_own of the group, head g_own
+  const int e_own = nl / G;
+  const int g_own = nl - e_own * G;
+  const int e_row = (4 * gr) / G;  // page of the PV result rows 4*gr .. 4*gr+3 held by this lane
+
+  f16x8 ONES;
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) ONES[sl] = static_cast<_Float16>(1.0f);
+  f16x8 BFAKE = zero8();
+  BFAKE[0] = BFAKE[1] = static_cast<_Float16>(1.0f);
+
+  float m_run = -INFINITY;   // column nl (QK layout)
+  float l_part = 0.f;        // this lane's tokens only; rows merged at the end
+  float acc[8][4];           // PV layout: row 4*gr + i, channel 16*nb + nl
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[nb][i] = 0.f;
+
+  const int gpw = groups_per_split / 4;
+  const int g_begin = sp * groups_per_split + wave * gpw;
+  const int g_end = min(g_begin + gpw, n_groups);
+  float* sb = lds + wave * (P * SC);
+  const int64_t pt_row = static_cast<int64_t>(s) * max_pages;
+  const int64_t head_off = static_cast<int64_t>(h) * R;
+
+  auto recs = [&](int gi, const uint8_t* (&rec)[P]) {
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const int pg = gi * P + e;
+      const int phys = page_table[pt_row + (pg < n_pages ? pg : gi * P)];
+      rec[e] = cache + static_cast<int64_t>(phys) * page_stride + head_off;
+    }
+  };
+
+  // One group: stage cur's scales in LDS, prefetch group gi+1 into nxt, compute gi from cur.
+  auto step = [&](Pair<KB, VB, P>& cur, Pair<KB, VB, P>& nxt, int gi) {
+#pragma unroll
+    for (int k = 0; k < 3 * P; ++k) reinterpret_cast<float4*>(sb)[lane + 64 * k] = cur.sc[k];
+    if (gi + 1 < g_end) {
+      const uint8_t* rec[P];
+      recs(gi + 1, rec);
+      load_pair<KB, VB, P>(nxt, rec, lane);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    const bool valid_own = gi * P + e_own < n_pages;
+    const float* sown = sb + e_own * SC;
+
+    // q'' = c_K ⊙ q' for this lane's page, as the QK B operand, split into fp16 hi + lo parts
+    // (q'' = hi + lo to ~22 bits) so that rounding q'' does not perturb the logits
+    f16x8 bqh[4], bql[4];
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const float4 c4 = *reinterpret_cast<const float4*>(sown + 4 * gr + 16 * e8);
+      const float4 q4 = *reinterpret_cast<const float4*>(&qrot[g_own][4 * gr + 16 * e8]);
+      const float x[4] = {c4.x * q4.x, c4.y * q4.y, c4.z * q4.z, c4.w * q4.w};
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl)
+        if (keperm<KB>(sl) == e8) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const _Float16 hi = static_cast<_Float16>(x[kb]);
+            bqh[kb][sl] = hi;
+            bql[kb][sl] = static_cast<_Float16>(x[kb] - static_cast<float>(hi));
+          }
+        }
+    }
+
+    // sigma_n = sum_j q''_nj (all rows of the result equal)
+    float sigma;
+    {
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        d = mfma16(ONES, bqh[kb], d);
+        d = mfma16(ONES, bql[kb], d);
+      }
+      sigma = d[0];
+    }
+
+    // QK: one accumulator per page; the lane keeps its own page's column
+    float lg[8][4];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      f32x4 d[P];
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        d[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const f16x8 a = dequant_k<KB>(cur.kq[e][mb], kb);
+          d[e] = mfma16(a, bqh[kb], d[e]);
+          d[e] = mfma16(a, bql[kb], d[e]);
+        }
+      }
+      f32x4 dd = d[0];
+#pragma unroll
+      for (int e = 1; e < P; ++e) dd = (e_own == e) ? d[e] : dd;
+      const float4 sk = *reinterpret_cast<const float4*>(sown + 128 + 16 * mb + 4 * gr);
+      const float4 mk = *reinterpret_cast<const float4*>(sown + 256 + 16 * mb + 4 * gr);
+      lg[mb][0] = fmaf(sk.x, dd[0], mk.x * sigma);
+      lg[mb][1] = fmaf(sk.y, dd[1], mk.y * sigma);
+      lg[mb][2] = fmaf(sk.z, dd[2], mk.z * sigma);
+      lg[mb][3] = fmaf(sk.w, dd[3], mk.w * sigma);
+    }
+
+    // online softmax for column nl
+    float mloc = -INFINITY;
+    if (valid_own) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, lg[mb][i]);
+    }
+    mloc = rows_max4(mloc);
+    const float m_new = fmaxf(m_run, mloc);
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+    m_run = m_new;
+
+    // PV weights w_t = p_t s'_t go to the MFMA in fp16.  Their rounding error enters u_j as
+    // sum_t (w~_t - w_t) q_tj; the zero-point term is corrected by -c0 sum_t (w~_t - w_t) with
+    // c0 = (2^b - 1)/2, which centres that error on the codes (q - c0 ~ q + m'/s').
+    constexpr float c0 = 0.5f * ((1 << VB) - 1);
+    f16x8 aw[4];
+    float msum = 0.f, psum = 0.f, wexact = 0.f, wround = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float wv[2][4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int mb = 2 * kb + hh;
+        const float4 sv = *reinterpret_cast<const float4*>(sown + 4 * 128 + 16 * mb + 4 * gr);
+        const float4 mv = *reinterpret_cast<const float4*>(sown + 5 * 128 + 16 * mb + 4 * gr);
+        const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
+        const float mvv[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = (live && valid_own) ? exp2f(lg[mb][i] - m_new) : 0.f;
+          psum += p;
+          msum = fmaf(p, mvv[i], msum);
+          wv[hh][i] = p * svv[i];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const _Float16 w0 = static_cast<_Float16>(wv[0][r]);
+        const _Float16 w1 = static_cast<_Float16>(wv[1][r]);
+        aw[kb][2 * r] = w0;
+        aw[kb][2 * r + 1] = w1;
+        wexact += wv[0][r] + wv[1][r];
+        wround += static_cast<float>(w0) + static_cast<float>(w1);
+      }
+    }
+    l_part = l_part * alpha + psum;
+    msum = fmaf(-c0, wround - wexact, msum);
+    // sum_t p_t m'_t enters the PV product as one extra k-step (hi/lo fp16 split)
+    f16x8 afake = zero8();
+    {
+      const _Float16 mh = static_cast<_Float16>(msum);
+      const _Float16 ml = static_cast<_Float16>(msum - static_cast<float>(mh));
+      afake[0] = mh;
+      afake[1] = ml;
+    }
+
+    // alpha of the PV rows 4*gr + i lives in lane 4*gr + i (any row of lanes)
+    float arow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * gr + i);
+    const float* srow = sb + e_row * SC;
+
+    // PV: one accumulator per page; the lane keeps its rows' page
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      f32x4 d[P];
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        d[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) d[e] = mfma16(aw[kb], dequant_v<VB>(cur.vq[e][nb], kb), d[e]);
+      }
+      f32x4 dd = d[0];
+#pragma unroll
+      for (int e = 1; e < P; ++e) dd = (e_row == e) ? d[e] : dd;
+      dd = mfma16(afake, BFAKE, dd);
+      const float cv = srow[3 * 128 + 16 * nb + nl];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv * dd[i]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  Pair<KB, VB, P> bufA, bufB;
+  if (g_begin < g_end) {
+    const uint8_t* rec[P];
+    recs(g_begin, rec);
+    load_pair<KB, VB, P>(bufA, rec, lane);
+  }
+  for (int gi = g_begin; gi < g_end; gi += 2) {
+    step(bufA, bufB, gi);
+    if (gi + 1 < g_end) step(bufB, bufA, gi + 1);
+  }
+
+  // ---- merge the 4 waves x P streams of each head, write one partial per head ----------
+  const float l_col = rows_sum4(l_part);
+  __syncthreads();  // staging buffers are reused below
+  float* mrg = lds + wave * 16 * MRG;
+  if (gr == 0) {
+    mrg[nl * MRG + 0] = m_run;
+    mrg[nl * MRG + 1] = l_col;
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mrg[(4 * gr + i) * MRG + 2 + 16 * nb + nl] = acc[nb][i];
+  __syncthreads();
+
+  for (int idx = tid; idx < G * kCh; idx += 256) {
+    const int g = idx >> 7, j = idx & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int e = 0; e < P; ++e) M = fmaxf(M, lds[(w * 16 + e * G + g) * MRG]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          const float* row = lds + (w * 16 + e * G + g) * MRG;
+          const float f = exp2f(row[0] - M);
+          L = fmaf(row[1], f, L);
+          A = fmaf(row[2 + j], f, A);
+        }
+    }
+    float* out = ws + ((static_cast<int64_t>(s) * num_q_heads + h * G + g) * n_splits + sp) * kPartialFloats;
+    if (j == 0) {
+      out[0] = M;
+      out[1] = L;
+    }
+    out[2 + j] = A;
+  }
+}
+
+// Merge the split-K partials with the fp16 tail, apply Hn once, normalise.
+// One workgroup per (sequence, kv head); 32 threads per query head, 4 channels each.
+template <int G>
+__global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict__ q, const float* __restrict__ ws,
+                                                     int n_splits, const int32_t* __restrict__ seq_lens,
+                                                     const _Float16* __restrict__ tail_k,
+                                                     const _Float16* __restrict__ tail_v, int num_q_heads,
+                                                     int num_kv_heads, float sm_log2e, _Float16* __restrict__ out) {
+  __shared__ float qs[G][kCh];
+  __shared__ float lg[G][kTok];
+  const int sh = blockIdx.x;
+  const int s = sh / num_kv_heads;
+  const int h = sh - s * num_kv_heads;
+  const int tid = threadIdx.x;
+  const int len = seq_lens[s];
+  const int nt = len & (kTok - 1);
+  const int64_t tail_base = static_cast<int64_t>(sh) * kTok * kCh;
+
+  for (int idx = tid; idx < G * kCh; idx += 256)
+    qs[idx >> 7][idx & 127] =
+        static_cast<float>(q[(static_cast<int64_t>(s) * num_q_heads + h * G) * kCh + idx]) * sm_log2e;
+  __syncthreads();
+  for (int idx = tid; idx < G * kTok; idx += 256) {
+    const int g = idx >> 7, t = idx & 127;
+    float d = -INFINITY;
+    if (t < nt) {
+      const _Float16* kr = tail_k + tail_base + t * kCh;
+      d = 0.f;
+      for (int j = 0; j < kCh; j += 8) {
+        const f16x8 kv = *reinterpret_cast<const f16x8*>(kr + j);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) d = fmaf(qs[g][j + c], static_cast<float>(kv[c]), d);
+      }
+    }
+    lg[g][t] = d;
+  }
+  __syncthreads();
+
+  const int r = tid & 31;
+  for (int g = tid >> 5; g < G; g += 8) {
+    const float* part = ws + (static_cast<int64_t>(s) * num_q_heads + h * G + g) * n_splits * kPartialFloats;
+    float M = -INFINITY;
+    for (int k = r; k < n_splits; k += 32) M = fmaxf(M, part[k * kPartialFloats]);
+    for (int t = r; t < nt; t += 32) M = fmaxf(M, lg[g][t]);
+#pragma unroll
+    for (int b = 16; b >= 1; b >>= 1) M = fmaxf(M, __shfl_xor(M, b, 32));
+    float L = 0.f;
+    float ar[4] = {0.f, 0.f, 0.f, 0.f}, aw[4] = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+      for (int k = r; k < n_splits; k += 32) {
+        const float mk = part[k * kPartialFloats];
+        if (mk != -INFINITY) L = fmaf(part[k * kPartialFloats + 1], exp2f(mk - M), L);
+      }
+      for (int t = r; t < nt; t += 32) L += exp2f(lg[g][t] - M);
+      for (int k = 0; k < n_splits; ++k) {
+        const float mk = part[k * kPartialFloats];
+        if (mk == -INFINITY) continue;
+        const float f = exp2f(mk - M);
+        const float4 a = *reinterpret_cast<const float4*>(part + k * kPartialFloats + 2 + 4 * r);
+        ar[0] = fmaf(a.x, f, ar[0]);
+        ar[1] = fmaf(a.y, f, ar[1]);
+        ar[2] = fmaf(a.z, f, ar[2]);
+        ar[3] = fmaf(a.w, f, ar[3]);
+      }
+      for (int t = 0; t < nt; ++t) {
+        const float f = exp2f(lg[g][t] - M);
+        const _Float16* vr = tail_v + tail_base + t * kCh + 4 * r;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) aw[c] = fmaf(f, static_cast<float>(vr[c]), aw[c]);
+      }
+    }
+#pragma unroll
+    for (int b = 16; b >= 1; b >>= 1) L += __shfl_xor(L, b, 32);
+    // Hn over the 128 rotated-domain channels (4 per thread: 2 stages in registers, 5 across lanes)
+    {
+      const float a0 = ar[0] + ar[1], a1 = ar[0] - ar[1], a2 = ar[2] + ar[3], a3 = ar[2] - ar[3];
+      ar[0] = a0 + a2;
+      ar[1] = a1 + a3;
+      ar[2] = a0 - a2;
+      ar[3] = a1 - a3;
+#pragma unroll
+      for (int b = 0; b < 5; ++b) {
+        const bool upper = (r >> b) & 1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float o = __shfl_xor(ar[c], 1 << b, 32);
+          ar[c] = upper ? o - ar[c] : ar[c] + o;
+        }
+      }
+    }
+    const float inv_l = L > 0.f ? 1.0f / L : 0.f;
+    constexpr float kInvSqrt128 = 0.08838834764831845f;
+    _Float16* o = out + (static_cast<int64_t>(s) * num_q_heads + h * G + g) * kCh + 4 * r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = static_cast<_Float16>((ar[c] * kInvSqrt128 + aw[c]) * inv_l);
+  }
+}
+
+DecodePlan plan_decode(int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq) {
+  DecodePlan p;
+  p.pages_per_group = 16 / group_size;
+  const int groups_max = (max_pages_per_seq + p.pages_per_group - 1) / p.pages_per_group;
+  const int units = num_seqs * num_kv_heads;
+  const int target_wgs = 512;  // 2 per CU on 256 CUs
+  int splits0 = units > 0 ? (target_wgs + units - 1) / units : 1;
+  if (splits0 < 1) splits0 = 1;
+  int gps = groups_max > 0 ? (groups_max + splits0 - 1) / splits0 : 1;
+  gps = ((gps + 3) / 4) * 4;  // whole groups per wave
+  if (gps < 4) gps = 4;
+  p.groups_per_split = gps;
+  p.n_splits = groups_max > 0 ? (groups_max + gps - 1) / gps : 1;
+  return p;
+}
+
+bool decode_supported(int kb, int vb, int group_size) {
+  return (kb == 4 || kb == 8) && (vb == 2 || vb == 8) && (group_size == 8 || group_size == 16);
+}
+
+template <int KB, int VB, int G>
+static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64_t page_stride,
+                                  const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                                  const _Float16* tail_k, const _Float16* tail_v, float sm_scale, _Float16* out,
+                                  float* workspace, int num_seqs, int num_q_heads, int num_kv_heads,
+                                  const DecodePlan& plan, hipStream_t stream) {
+  const float qscale = sm_scale * kLog2e * 0.08838834764831845f;
+  hipLaunchKernelGGL((decode_kernel<KB, VB, G>), dim3(num_seqs * num_kv_heads, plan.n_splits), dim3(256), 0, stream, q,
+                     cache, page_stride, page_table, max_pages, seq_lens, num_q_heads, num_kv_heads, qscale, workspace,
+                     plan.n_splits, plan.groups_per_split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((combine_kernel<G>), dim3(num_seqs * num_kv_heads), dim3(256), 0, stream, q, workspace,
+                     plan.n_splits, seq_lens, tail_k, tail_v, num_q_heads, num_kv_heads, sm_scale * kLog2e, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(int kb, int vb, int group_size, const _Float16* q, const uint8_t* cache, int64_t page_stride,
+                         const int32_t* page_table, int max_pages, const int32_t* seq_lens, const _Float16* tail_k,
+                         const _Float16* tail_v, float sm_scale, _Float16* out, float* workspace, int num_seqs,
+                         int num_q_heads, int num_kv_heads, const DecodePlan& plan, hipStream_t stream) {
+  if (num_seqs == 0) return hipSuccess;
+#define KVARN_DECODE_CASE(KB_, VB_, G_)                                                                          \
+  if (kb == KB_ && vb == VB_ && group_size == G_)                                                                \
+    return launch_decode_t<KB_, VB_, G_>(q, cache, page_stride, page_table, max_pages, seq_lens, tail_k, tail_v, \
+                                         sm_scale, out, workspace, num_seqs, num_q_heads, num_kv_heads, plan, stream);
+  KVARN_DECODE_CASE(4, 2, 8)
+  KVARN_DECODE_CASE(8, 8, 8)
+  KVARN_DECODE_CASE(4, 8, 8)
+  KVARN_DECODE_CASE(8, 2, 8)
+  KVARN_DECODE_CASE(4, 2, 16)
+  KVARN_DECODE_CASE(8, 8, 16)
+  KVARN_DECODE_CASE(4, 8, 16)
+  KVARN_DECODE_CASE(8, 2, 16)
+#undef KVARN_DECODE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvarn

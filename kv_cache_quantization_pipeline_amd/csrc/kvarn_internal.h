@@ -1,0 +1,37 @@
+// Kernel launchers behind the libkvarn C-ABI (host-side declarations).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvarn {
+
+hipError_t launch_quantize_tiles(const _Float16* k, const _Float16* v, const int32_t* dst_pages, uint8_t* cache,
+                                 int64_t page_stride, int num_tiles, int num_kv_heads, int kb, int vb, int iters,
+                                 hipStream_t stream);
+
+hipError_t launch_append(const _Float16* k_new, const _Float16* v_new, int32_t* seq_lens, _Float16* tail_k,
+                         _Float16* tail_v, const int32_t* page_table, int max_pages, uint8_t* cache,
+                         int64_t page_stride, int num_seqs, int num_kv_heads, int kb, int vb, int iters,
+                         hipStream_t stream);
+
+// Split-K decode plan: the grid is (num_seqs*num_kv_heads, n_splits) workgroups of 4 waves;
+// a split covers groups_per_split groups of P = 16/G pages, groups_per_split / 4 per wave.
+struct DecodePlan {
+  int pages_per_group;
+  int groups_per_split;
+  int n_splits;
+};
+DecodePlan plan_decode(int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq);
+
+// Workspace floats per (sequence, query head, split): running max, running sum, 128 accumulators.
+constexpr int kPartialFloats = 130;
+
+bool decode_supported(int kb, int vb, int group_size);
+
+hipError_t launch_decode(int kb, int vb, int group_size, const _Float16* q, const uint8_t* cache, int64_t page_stride,
+                         const int32_t* page_table, int max_pages, const int32_t* seq_lens, const _Float16* tail_k,
+                         const _Float16* tail_v, float sm_scale, _Float16* out, float* workspace, int num_seqs,
+                         int num_q_heads, int num_kv_heads, const DecodePlan& plan, hipStream_t stream);
+
+}  // namespace kvarn

@@ -1,0 +1,162 @@
+// libkvarn C-ABI: argument validation and kernel launches (see include/libkvarn.h).
+#include "../../include/libkvarn.h"
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kvarn_device.h"
+#include "kvarn_internal.h"
+
+namespace {
+
+bool bits_ok(int b) { return b == 2 || b == 4 || b == 8; }
+
+kvarn_status check_format(const kvarn_format* f) {
+  if (f == nullptr) return KVARN_E_INVALID_ARG;
+  if (!bits_ok(f->k_bits) || !bits_ok(f->v_bits)) return KVARN_E_UNSUPPORTED;
+  if (f->group != 128 || f->head_dim != 128 || f->block_size != 128) return KVARN_E_UNSUPPORTED;
+  if (f->sinkhorn_iters < 0 || f->sinkhorn_iters > 64) return KVARN_E_INVALID_ARG;
+  return KVARN_OK;
+}
+
+// parse a decimal integer at *p, advancing p; false if none
+bool parse_int(const char*& p, int* out) {
+  if (*p < '0' || *p > '9') return false;
+  long v = 0;
+  while (*p >= '0' && *p <= '9') {
+    v = v * 10 + (*p - '0');
+    if (v > 1000000) return false;
+    ++p;
+  }
+  *out = static_cast<int>(v);
+  return true;
+}
+
+kvarn_status hip_status(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+kvarn_status kvarn_format_parse(const char* name, kvarn_format* out) {
+  if (name == nullptr || out == nullptr) return KVARN_E_INVALID_ARG;
+  const char* p = name;
+  const char* prefix = "kvarn_k";
+  if (std::strncmp(p, prefix, std::strlen(prefix)) != 0) return KVARN_E_INVALID_ARG;
+  p += std::strlen(prefix);
+  int kb, vb, g;
+  if (!parse_int(p, &kb)) return KVARN_E_INVALID_ARG;
+  if (*p++ != 'v') return KVARN_E_INVALID_ARG;
+  if (!parse_int(p, &vb)) return KVARN_E_INVALID_ARG;
+  if (*p++ != '_' || *p++ != 'g') return KVARN_E_INVALID_ARG;
+  if (!parse_int(p, &g)) return KVARN_E_INVALID_ARG;
+  if (*p != '\0') return KVARN_E_INVALID_ARG;
+  kvarn_format f{kb, vb, g, 128, 128, 8};
+  const kvarn_status st = check_format(&f);
+  if (st != KVARN_OK) return st;
+  *out = f;
+  return KVARN_OK;
+}
+
+kvarn_status kvarn_format_check(const kvarn_format* f) { return check_format(f); }
+
+size_t kvarn_record_bytes(const kvarn_format* f) {
+  if (check_format(f) != KVARN_OK) return 0;
+  return static_cast<size_t>(kvarn::record_bytes(f->k_bits, f->v_bits));
+}
+
+size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t max_pages_per_seq) {
+  if (check_format(f) != KVARN_OK || num_seqs < 0 || num_kv_heads <= 0 || num_q_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || max_pages_per_seq < 0)
+    return 0;
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 8 && G != 16) return 0;
+  const kvarn::DecodePlan plan = kvarn::plan_decode(num_seqs, num_kv_heads, G, max_pages_per_seq);
+  return static_cast<size_t>(num_seqs) * num_q_heads * plan.n_splits * kvarn::kPartialFloats * sizeof(float);
+}
+
+kvarn_status kvarn_quantize_tiles(const kvarn_format* f, int32_t num_tiles, int32_t num_kv_heads, const void* k,
+                                  const void* v, const int32_t* dst_pages, void* cache, int64_t page_stride_bytes,
+                                  hipStream_t stream) {
+  const kvarn_status st = check_format(f);
+  if (st != KVARN_OK) return st;
+  if (num_tiles < 0 || num_kv_heads <= 0) return KVARN_E_INVALID_ARG;
+  if (num_tiles == 0) return KVARN_OK;
+  if (k == nullptr || v == nullptr || dst_pages == nullptr || cache == nullptr) return KVARN_E_INVALID_ARG;
+  const int64_t R = kvarn::record_bytes(f->k_bits, f->v_bits);
+  if (page_stride_bytes < R * num_kv_heads || page_stride_bytes % 16 != 0) return KVARN_E_INVALID_ARG;
+  if (static_cast<int64_t>(num_tiles) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
+  return hip_status(kvarn::launch_quantize_tiles(static_cast<const _Float16*>(k), static_cast<const _Float16*>(v),
+                                                 dst_pages, static_cast<uint8_t*>(cache), page_stride_bytes, num_tiles,
+                                                 num_kv_heads, f->k_bits, f->v_bits, f->sinkhorn_iters, stream));
+}
+
+kvarn_status kvarn_append_token(const kvarn_format* f, int32_t num_seqs, int32_t num_kv_heads, const void* k_new,
+                                const void* v_new, int32_t* seq_lens, void* tail_k, void* tail_v,
+                                const int32_t* page_table, int32_t max_pages_per_seq, void* cache,
+                                int64_t page_stride_bytes, hipStream_t stream) {
+  const kvarn_status st = check_format(f);
+  if (st != KVARN_OK) return st;
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0) return KVARN_E_INVALID_ARG;
+  if (num_seqs == 0) return KVARN_OK;
+  if (k_new == nullptr || v_new == nullptr || seq_lens == nullptr || tail_k == nullptr || tail_v == nullptr ||
+      page_table == nullptr || cache == nullptr)
+    return KVARN_E_INVALID_ARG;
+  const int64_t R = kvarn::record_bytes(f->k_bits, f->v_bits);
+  if (page_stride_bytes < R * num_kv_heads || page_stride_bytes % 16 != 0) return KVARN_E_INVALID_ARG;
+  if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
+  return hip_status(kvarn::launch_append(
+      static_cast<const _Float16*>(k_new), static_cast<const _Float16*>(v_new), seq_lens,
+      static_cast<_Float16*>(tail_k), static_cast<_Float16*>(tail_v), page_table, max_pages_per_seq,
+      static_cast<uint8_t*>(cache), page_stride_bytes, num_seqs, num_kv_heads, f->k_bits, f->v_bits,
+      f->sinkhorn_iters, stream));
+}
+
+kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, const void* q, const void* cache, int64_t page_stride_bytes,
+                                    const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                    const void* tail_k, const void* tail_v, float sm_scale, void* out,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const kvarn_status st = check_format(f);
+  if (st != KVARN_OK) return st;
+  if (num_seqs < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_pages_per_seq < 0) return KVARN_E_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return KVARN_E_INVALID_ARG;
+  const int G = num_q_heads / num_kv_heads;
+  if (!kvarn::decode_supported(f->k_bits, f->v_bits, G)) return KVARN_E_UNSUPPORTED;
+  if (num_seqs == 0) return KVARN_OK;
+  if (q == nullptr || cache == nullptr || page_table == nullptr || seq_lens == nullptr || tail_k == nullptr ||
+      tail_v == nullptr || out == nullptr || workspace == nullptr)
+    return KVARN_E_INVALID_ARG;
+  const int64_t R = kvarn::record_bytes(f->k_bits, f->v_bits);
+  if (page_stride_bytes < R * num_kv_heads || page_stride_bytes % 16 != 0) return KVARN_E_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return KVARN_E_INVALID_ARG;
+  if (workspace_bytes < kvarn_decode_workspace_bytes(f, num_seqs, num_q_heads, num_kv_heads, max_pages_per_seq))
+    return KVARN_E_INVALID_ARG;
+  if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
+  const kvarn::DecodePlan plan = kvarn::plan_decode(num_seqs, num_kv_heads, G, max_pages_per_seq);
+  if (plan.n_splits > 65535) return KVARN_E_UNSUPPORTED;
+  return hip_status(kvarn::launch_decode(f->k_bits, f->v_bits, G, static_cast<const _Float16*>(q),
+                                         static_cast<const uint8_t*>(cache), page_stride_bytes, page_table,
+                                         max_pages_per_seq, seq_lens, static_cast<const _Float16*>(tail_k),
+                                         static_cast<const _Float16*>(tail_v), sm_scale, static_cast<_Float16*>(out),
+                                         static_cast<float*>(workspace), num_seqs, num_q_heads, num_kv_heads, plan,
+                                         stream));
+}
+
+const char* kvarn_status_string(kvarn_status s) {
+  switch (s) {
+    case KVARN_OK:
+      return "ok";
+    case KVARN_E_INVALID_ARG:
+      return "invalid argument";
+    case KVARN_E_UNSUPPORTED:
+      return "unsupported";
+    case KVARN_E_HIP:
+      return "HIP error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

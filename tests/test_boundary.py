@@ -1,0 +1,115 @@
+"""CPU tests of the libkvarn C-ABI: the library loads, exports every symbol the
+header declares, parses formats, sizes records and workspaces, and rejects bad
+arguments with a status before any launch (no GPU needed for these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_quantization_pipeline_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "libkvarn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvarn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_header_symbol():
+    names = _header_functions()
+    assert set(names) == set(kv.EXPORTS), names
+    L = kv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("name,expect", [
+    ("kvarn_k4v2_g128", (4, 2, 128, 128, 128, 8)),
+    ("kvarn_k8v8_g128", (8, 8, 128, 128, 128, 8)),
+    ("kvarn_k2v4_g128", (2, 4, 128, 128, 128, 8)),
+])
+def test_format_parse(name, expect):
+    f = kv.format_parse(name)
+    assert (f.k_bits, f.v_bits, f.group, f.head_dim, f.block_size, f.sinkhorn_iters) == expect
+
+
+@pytest.mark.parametrize("name,status", [
+    ("kvarn_k4v2_g64", kv.KVARN_E_UNSUPPORTED),
+    ("kvarn_k3v2_g128", kv.KVARN_E_UNSUPPORTED),
+    ("kvarn_k4v16_g128", kv.KVARN_E_UNSUPPORTED),
+    ("kvarn_k4v2", kv.KVARN_E_INVALID_ARG),
+    ("kvarn_k4v2_g128x", kv.KVARN_E_INVALID_ARG),
+    ("int4", kv.KVARN_E_INVALID_ARG),
+    ("", kv.KVARN_E_INVALID_ARG),
+])
+def test_format_parse_rejects(name, status):
+    with pytest.raises(kv.KvarnError) as ei:
+        kv.format_parse(name)
+    assert ei.value.status == status
+
+
+def test_record_and_workspace_sizes():
+    f = kv.format_parse("kvarn_k4v2_g128")
+    assert kv.record_bytes(f) == 15360
+    assert kv.record_bytes(kv.format_parse("kvarn_k8v8_g128")) == 35840
+    ws = kv.decode_workspace_bytes(f, 32, 32, 4, 128)
+    assert ws > 0 and ws % (130 * 4) == 0
+    assert kv.decode_workspace_bytes(f, 32, 24, 4, 128) == 0   # G = 6 unsupported
+    assert kv.decode_workspace_bytes(f, 32, 30, 4, 128) == 0   # Hq % Hkv != 0
+    bad = kv.Format(4, 2, 128, 64, 128, 8)
+    assert kv.record_bytes(bad) == 0
+    assert kv.lib().kvarn_format_check(ctypes.byref(bad)) == kv.KVARN_E_UNSUPPORTED
+    assert kv.lib().kvarn_format_check(ctypes.byref(kv.Format(4, 2, 128, 128, 256, 8))) == kv.KVARN_E_UNSUPPORTED
+    assert kv.lib().kvarn_format_check(ctypes.byref(kv.Format(4, 2, 128, 128, 128, -1))) == kv.KVARN_E_INVALID_ARG
+    assert kv.lib().kvarn_format_check(None) == kv.KVARN_E_INVALID_ARG
+
+
+def test_calls_reject_bad_arguments_before_launch():
+    L = kv.lib()
+    f = kv.format_parse("kvarn_k4v2_g128")
+    fp = ctypes.byref(f)
+    dummy = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+    R = 15360
+    # quantize: null pointers, negative sizes, short page stride, unaligned stride
+    assert L.kvarn_quantize_tiles(fp, 4, 2, None, dummy, dummy, dummy, 2 * R, None) == kv.KVARN_E_INVALID_ARG
+    assert L.kvarn_quantize_tiles(fp, -1, 2, dummy, dummy, dummy, dummy, 2 * R, None) == kv.KVARN_E_INVALID_ARG
+    assert L.kvarn_quantize_tiles(fp, 4, 0, dummy, dummy, dummy, dummy, 2 * R, None) == kv.KVARN_E_INVALID_ARG
+    assert L.kvarn_quantize_tiles(fp, 4, 2, dummy, dummy, dummy, dummy, 2 * R - 16, None) == kv.KVARN_E_INVALID_ARG
+    assert L.kvarn_quantize_tiles(fp, 4, 2, dummy, dummy, dummy, dummy, 2 * R + 8, None) == kv.KVARN_E_INVALID_ARG
+    assert L.kvarn_quantize_tiles(None, 4, 2, dummy, dummy, dummy, dummy, 2 * R, None) == kv.KVARN_E_INVALID_ARG
+    assert L.kvarn_quantize_tiles(fp, 0, 2, None, None, None, None, 0, None) == kv.KVARN_OK   # empty: no work
+    g64 = kv.Format(4, 2, 64, 128, 128, 8)
+    assert L.kvarn_quantize_tiles(ctypes.byref(g64), 4, 2, dummy, dummy, dummy, dummy, 2 * R, None) \
+        == kv.KVARN_E_UNSUPPORTED
+    # append
+    assert L.kvarn_append_token(fp, 2, 2, dummy, dummy, None, dummy, dummy, dummy, 4, dummy, 2 * R, None) \
+        == kv.KVARN_E_INVALID_ARG
+    assert L.kvarn_append_token(fp, 2, 2, dummy, dummy, dummy, dummy, dummy, dummy, 0, dummy, 2 * R, None) \
+        == kv.KVARN_E_INVALID_ARG
+    assert L.kvarn_append_token(fp, 0, 2, None, None, None, None, None, None, 4, None, 2 * R, None) == kv.KVARN_OK
+    # decode: GQA ratio, workspace size / alignment, nulls
+    ws_need = kv.decode_workspace_bytes(f, 2, 16, 2, 4)
+    args = dict(q=dummy, cache=dummy, pt=dummy, sl=dummy, tk=dummy, tv=dummy, out=dummy, ws=dummy)
+
+    def dec(nseq=2, hq=16, hkv=2, stride=2 * R, ws=dummy, wsb=ws_need, q=dummy, fmt=fp):
+        return L.kvarn_decode_attention(fmt, nseq, hq, hkv, q, dummy, stride, dummy, 4, dummy, dummy, dummy,
+                                        0.1, dummy, ws, wsb, None)
+    assert dec(hq=15) == kv.KVARN_E_INVALID_ARG
+    assert dec(hq=12, hkv=2) == kv.KVARN_E_UNSUPPORTED     # G = 6
+    assert dec(hq=8, hkv=2) == kv.KVARN_E_UNSUPPORTED      # G = 4
+    assert dec(wsb=ws_need - 1) == kv.KVARN_E_INVALID_ARG
+    assert dec(ws=ctypes.c_void_p(0x1004)) == kv.KVARN_E_INVALID_ARG
+    assert dec(q=None) == kv.KVARN_E_INVALID_ARG
+    assert dec(stride=R) == kv.KVARN_E_INVALID_ARG
+    assert dec(fmt=ctypes.byref(kv.format_parse("kvarn_k2v4_g128"))) == kv.KVARN_E_UNSUPPORTED
+    assert dec(nseq=0) == kv.KVARN_OK
+    del args
+
+
+def test_status_strings():
+    assert kv.status_string(0) == "ok"
+    assert kv.status_string(3) == "HIP error"
+    assert kv.status_string(99) == "unknown status"
