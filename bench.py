@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the KVarN hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. kvarn_quantize_tiles   bulk quantise 1024 tiles x 4 kv heads (8 sequences x 16384 tokens, the
+                            kv-head share of a Qwen3-32B-shaped layer at TP=2), k4v2 g128, pages permuted
+  2. kvarn_append_token     one new token for each of 32 sequences x 4 kv heads (fp16 tail; a tail that
+                            fills is quantised inline)
+  3. kvarn_decode_attention decode for 32 sequences at 16384+ tokens, 32 query / 4 kv heads, over the
+                            k4v2 paged cache plus the fp16 tails (decode + combine kernels)
+Inputs are resident in HBM before the timed region.  Two copies of every input and cache are used
+alternately, so each kernel's reads come from HBM, not from the 256 MB Infinity Cache.
+
+Prints one JSON line.  value = algorithmic bytes of the step / step time (GB/s); the per-kernel
+numbers (quantize GB/s, decode tokens/s, fractions of the 8 TB/s HBM peak) are in "kernels".
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+FORMAT = "kvarn_k4v2_g128"
+
+# workload sizes (see kv_cache_quantization_pipeline_amd/synth.py WORKLOADS)
+Q_TILES, Q_HKV = 1024, 4                 # bulk quantise
+D_B, D_CTX, D_HQ, D_HKV = 32, 16384, 32, 4  # decode
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="wall seconds per oracle leg (quantise, decode) of the CPU baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (for scaling PMC byte counters)")
+    return ap.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_quantization_pipeline_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(src_hash):
+    """HBM bytes per launch from committed rocprofv3 PMC runs, only if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != src_hash:
+        return {}
+    return t.get("kernels", {})
+
+
+def cpu_baseline(k1, v1, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload: whole sequences of the
+    bulk-quantise batch, then decode steps over oracle-quantised sequences of the decode shape."""
+    import numpy as np
+
+    import oracle
+    from kv_cache_quantization_pipeline_amd import synth
+
+    threads = oracle.threads_used(0)
+    R = oracle.record_bytes(4, 2)
+    # quantise leg: one sequence (128 tiles x 4 heads) at a time until `seconds` have passed
+    q_bytes, q_time, q_seqs = 0, 0.0, 0
+    kt = k1.reshape(-1, 128, Q_HKV, 128)
+    vt = v1.reshape(-1, 128, Q_HKV, 128)
+    cache = np.zeros(128 * Q_HKV * R, np.uint8)
+    pages = np.arange(128, dtype=np.int32)
+    while q_time < seconds and q_seqs < kt.shape[0] // 128:
+        s0 = q_seqs * 128
+        t0 = time.perf_counter()
+        oracle.quantize_tiles(4, 2, 8, kt[s0:s0 + 128].view(np.uint16), vt[s0:s0 + 128].view(np.uint16), pages,
+                              cache, Q_HKV * R, nthreads=threads)
+        q_time += time.perf_counter() - t0
+        q_bytes += 128 * Q_HKV * (2 * 128 * 128 * 2 + R)
+        q_seqs += 1
+    # decode leg: the sequence just quantised, decoded with 32 query heads, repeated until `seconds`
+    q = synth.gen_q(2, 1, D_HQ)
+    pt = pages[None, :]
+    lens = np.array([128 * 128], np.int32)
+    tail = np.zeros((1, Q_HKV, 128, 128), np.uint16)
+    d_bytes, d_time, d_calls = 0, 0.0, 0
+    while d_time < seconds:
+        t0 = time.perf_counter()
+        oracle.decode_attention(4, 2, q.view(np.uint16), cache, Q_HKV * R, pt, lens, tail, tail,
+                                1 / math.sqrt(128), Q_HKV, nthreads=threads)
+        d_time += time.perf_counter() - t0
+        d_bytes += 128 * Q_HKV * R + 2 * D_HQ * 256
+        d_calls += 1
+    rate = (q_bytes + d_bytes) / (q_time + d_time) / 1e9
+    return {"value": rate, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{q_seqs} sequence(s) of 128 tiles x 4 kv heads quantised ({q_bytes / 1e6:.1f} MB, "
+                       f"{q_time:.1f} s) + {d_calls} decode call(s) of 1 sequence x 16384 tokens x 32 query "
+                       f"heads ({d_bytes / 1e6:.1f} MB, {d_time:.1f} s); fp64 oracle, {threads} threads"),
+            "quantize_GBps": q_bytes / q_time / 1e9, "decode_tokens_per_s": d_calls / d_time}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU; the method needs no cross-GPU exchange "
+              "(kv heads and sequences shard independently), so runs with --gpus > 1 are not provided.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_quantization_pipeline_amd as kv
+    from kv_cache_quantization_pipeline_amd import synth
+
+    dev = torch.device("cuda:0")
+    fmt = kv.format_parse(FORMAT)
+    R = kv.record_bytes(fmt)
+    t_prep = time.perf_counter()
+
+    # ---- bulk quantise inputs (two copies) -------------------------------------------------
+    w1 = synth.WORKLOADS["bulk_quantize_qwen3_32b_tp2"]
+    k1, v1 = synth.gen_kv(w1["seed"], w1["batch"] * w1["ctx"], w1["n_kv_heads"])
+    pages1 = torch.from_numpy(synth.gen_page_perm(w1["seed"], Q_TILES)).to(dev)
+    k1d = [torch.from_numpy(synth.tiles_view(k1)).to(dev)]
+    v1d = [torch.from_numpy(synth.tiles_view(v1)).to(dev)]
+    k1d.append(k1d[0].clone())
+    v1d.append(v1d[0].clone())
+    stride1 = Q_HKV * R
+    cache1 = [torch.zeros(Q_TILES * stride1, dtype=torch.uint8, device=dev) for _ in range(2)]
+
+    # ---- decode cache: quantise the decode workload's K/V once (untimed), two copies ----------
+    w2 = synth.WORKLOADS["decode_gqa8_b32_ctx16k"]
+    pages_per_seq = D_CTX // 128
+    extra = 4                                   # pages for tails that fill during the run
+    max_pages = pages_per_seq + extra
+    n_pool = D_B * max_pages
+    perm2 = synth.gen_page_perm(w2["seed"], n_pool).reshape(D_B, max_pages)
+    pt2 = torch.from_numpy(np.ascontiguousarray(perm2)).to(dev)
+    stride2 = D_HKV * R
+    k2, v2 = synth.gen_kv(w2["seed"], D_B * D_CTX, D_HKV)
+    k2d = torch.from_numpy(synth.tiles_view(k2)).to(dev)
+    v2d = torch.from_numpy(synth.tiles_view(v2)).to(dev)
+    del k2, v2
+    dst2 = torch.from_numpy(np.ascontiguousarray(perm2[:, :pages_per_seq]).reshape(-1)).to(dev)
+    cache2 = []
+    for _ in range(2):
+        c = torch.zeros(n_pool * stride2, dtype=torch.uint8, device=dev)
+        kv.quantize_tiles(fmt, k2d, v2d, dst2, c, stride2)
+        cache2.append(c)
+    del k2d, v2d
+    rng = np.random.default_rng(w2["seed"] + 7)
+    knew = torch.from_numpy((rng.standard_normal((D_B, D_HKV, 128)) * 1.5).astype(np.float16)).to(dev)
+    vnew = torch.from_numpy((rng.standard_normal((D_B, D_HKV, 128)) * 1.5).astype(np.float16)).to(dev)
+    lens2 = [torch.full((D_B,), D_CTX, dtype=torch.int32, device=dev) for _ in range(2)]
+    tails = [(torch.zeros(D_B, D_HKV, 128, 128, dtype=torch.float16, device=dev),
+              torch.zeros(D_B, D_HKV, 128, 128, dtype=torch.float16, device=dev)) for _ in range(2)]
+    q2 = torch.from_numpy(synth.gen_q(w2["seed"], D_B, D_HQ)).to(dev)
+    out2 = torch.empty(D_B, D_HQ, 128, dtype=torch.float16, device=dev)
+    wsb = kv.decode_workspace_bytes(fmt, D_B, D_HQ, D_HKV, max_pages)
+    ws2 = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=dev)
+    sm = 1.0 / math.sqrt(128)
+    torch.cuda.synchronize(dev)
+    prep_s = time.perf_counter() - t_prep
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
+
+    # host-side mirror of the decode lengths, for the algorithmic byte count of each step
+    host_lens = [np.full(D_B, D_CTX, np.int64) for _ in range(2)]
+
+    def decode_bytes(lens):
+        full = lens // 128
+        tail = lens % 128
+        return int((full * D_HKV * R).sum() + (tail * D_HKV * 2 * 256).sum() + D_B * D_HQ * 256 * 2)
+
+    def append_bytes(lens_before):
+        fills = int(((lens_before + 1) % 128 == 0).sum())
+        base = D_B * D_HKV * (2 * 256 + 2 * 256) + D_B * 8
+        return base + fills * D_HKV * (2 * 128 * 128 * 2 + R)
+
+    quant_bytes = Q_TILES * Q_HKV * (2 * 128 * 128 * 2 + R)
+    ev = []
+
+    def step(i, record):
+        c = i % 2
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record()
+        kv.quantize_tiles(fmt, k1d[c], v1d[c], pages1, cache1[c], stride1)
+        if record:
+            e[1].record()
+        kv.append_token(fmt, knew, vnew, lens2[c], tails[c][0], tails[c][1], pt2, cache2[c], stride2)
+        if record:
+            e[2].record()
+        kv.decode_attention(fmt, q2, cache2[c], stride2, pt2, lens2[c], tails[c][0], tails[c][1], sm, out2, ws2,
+                            D_HKV)
+        if record:
+            e[3].record()
+            ev.append(e)
+        b_app = append_bytes(host_lens[c])
+        host_lens[c] += 1
+        return b_app, decode_bytes(host_lens[c])
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize(dev)
+    bytes_app = bytes_dec = 0
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        ba, bd = step(i, True)
+        bytes_app += ba
+        bytes_dec += bd
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    assert torch.isfinite(out2.float()).all().item()
+
+    tq = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev) * 1e-3
+    ta = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev) * 1e-3
+    td = sum(e[2].elapsed_time(e[3]) for e in ev) / len(ev) * 1e-3
+    step_s = elapsed / args.steps
+    total_bytes = quant_bytes * args.steps + bytes_app + bytes_dec
+    value = total_bytes / elapsed / 1e9
+    dec_b = bytes_dec / args.steps
+    app_b = bytes_app / args.steps
+
+    src_hash = source_hash()
+    traffic = load_traffic(src_hash)
+    kernels = {
+        "quantize_tiles": {"GBps": quant_bytes / tq / 1e9, "frac_hbm": quant_bytes / tq / 1e9 / HBM_PEAK_GBPS,
+                           "us": tq * 1e6, "bytes": quant_bytes, "tile_heads": Q_TILES * Q_HKV},
+        "append_token": {"us": ta * 1e6, "bytes": app_b, "GBps": app_b / ta / 1e9},
+        "decode_attention": {"GBps": dec_b / td / 1e9, "frac_hbm": dec_b / td / 1e9 / HBM_PEAK_GBPS,
+                             "us": td * 1e6, "bytes": dec_b, "tokens_per_s": D_B / td,
+                             "note": "decode + combine kernels; one layer call, 1 token per sequence"},
+    }
+    dom = "quantize_tiles" if tq >= td else "decode_attention"
+    dk = kernels[dom]
+    tr = traffic.get(dom)
+    roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": dk["GBps"] / HBM_PEAK_GBPS, "traffic": tr, "kernel": dom,
+                "algorithmic_bytes_per_launch": dk["bytes"]}
+
+    result = {
+        "metric": "quantize GB/s + quantized decode-attn tokens/s, % of HBM peak (k4v2 g128)",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": ("bulk quantize 1024 tiles x 4 kv heads (8 seqs x 16384 tokens) + append 1 token "
+                                "x 32 seqs + decode 32 seqs x 16384 ctx, 32 q / 4 kv heads, head_dim 128, "
+                                "kvarn_k4v2_g128, block 128, 8 Sinkhorn iterations"),
+                   "format": FORMAT, "quantize_tiles": Q_TILES, "kv_heads": Q_HKV, "decode_batch": D_B,
+                   "decode_ctx": D_CTX, "q_heads": D_HQ, "parallelism": "single GPU"},
+        "frac_hbm_step": value / HBM_PEAK_GBPS,
+        "kernels": kernels,
+        "roofline": roofline,
+        "source_hash": src_hash,
+        "prep_s": prep_s,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(k1, v1, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
