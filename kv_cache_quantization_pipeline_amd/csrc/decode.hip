@@ -152,18 +152,24 @@ __device__ __forceinline__ void load_pair(Pair<KB, VB, P>& d, const uint8_t* con
   constexpr int SOFF = scale_offset(KB, VB);
   const int nl = lane & 15, gr = lane >> 4;
 #pragma unroll
-  for (int e = 0; e < P; ++e) {
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) load_k<KB>(d.kq[e][mb], rec[e] + (16 * mb + nl) * 16 * KB + 4 * gr * KB);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      load_v<VB>(d.vq[e][nb], rec[e] + k_code_bytes(KB) + ((nb * 4 + gr) * 16 + nl) * 4 * VB);
-  }
-#pragma unroll
   for (int k = 0; k < 3 * P; ++k) {
     const int c = lane + 64 * k;
     d.sc[k] = *reinterpret_cast<const float4*>(rec[c / 192] + SOFF + (c % 192) * 16);
   }
+#pragma unroll
+  for (int e = 0; e < P; ++e)
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) load_k<KB>(d.kq[e][mb], rec[e] + (16 * mb + nl) * 16 * KB + 4 * gr * KB);
+}
+
+template <int KB, int VB, int P>
+__device__ __forceinline__ void load_pair_v(Pair<KB, VB, P>& d, const uint8_t* const (&rec)[P], int lane) {
+  const int nl = lane & 15, gr = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < P; ++e)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      load_v<VB>(d.vq[e][nb], rec[e] + k_code_bytes(KB) + ((nb * 4 + gr) * 16 + nl) * 4 * VB);
 }
 
 __device__ __forceinline__ f16x8 zero8() {
@@ -173,7 +179,7 @@ __device__ __forceinline__ f16x8 zero8() {
 }  // namespace
 
 template <int KB, int VB, int G>
-__global__ __launch_bounds__(256, 1) void decode_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ cache,
+__global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ cache,
                                                         int64_t page_stride, const int32_t* __restrict__ page_table,
                                                         int max_pages, const int32_t* __restrict__ seq_lens,
                                                         int num_q_heads, int num_kv_heads, float qscale,
@@ -259,15 +265,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const _Float16* __restri
     }
   };
 
-  // One group: stage cur's scales in LDS, prefetch group gi+1 into nxt, compute gi from cur.
-  auto step = [&](Pair<KB, VB, P>& cur, Pair<KB, VB, P>& nxt, int gi) {
+  // One group: load its codes and scales, stage the scales in LDS, compute.  Two waves share
+  // each SIMD, so one wave's loads overlap the other's arithmetic.
+  auto step = [&](int gi) {
+    Pair<KB, VB, P> cur;
+    const uint8_t* rec[P];
+    recs(gi, rec);
+    load_pair<KB, VB, P>(cur, rec, lane);
 #pragma unroll
     for (int k = 0; k < 3 * P; ++k) reinterpret_cast<float4*>(sb)[lane + 64 * k] = cur.sc[k];
-    if (gi + 1 < g_end) {
-      const uint8_t* rec[P];
-      recs(gi + 1, rec);
-      load_pair<KB, VB, P>(nxt, rec, lane);
-    }
     __builtin_amdgcn_wave_barrier();
 
     const bool valid_own = gi * P + e_own < n_pages;
@@ -331,6 +337,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const _Float16* __restri
       lg[mb][3] = fmaf(sk.w, dd[3], mk.w * sigma);
     }
 
+    // V codes are loaded only now, so that they are not live during QK (register budget of two
+    // waves per SIMD); the softmax below covers part of their latency
+    __builtin_amdgcn_sched_barrier(0);
+    load_pair_v<KB, VB, P>(cur, rec, lane);
+
     // online softmax for column nl
     float mloc = -INFINITY;
     if (valid_own) {
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const _Float16* __restri
     mloc = rows_max4(mloc);
     const float m_new = fmaxf(m_run, mloc);
     const bool live = m_new != -INFINITY;
-    const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+    const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = m_new;
 
     // PV weights w_t = p_t s'_t go to the MFMA in fp16.  Their rounding error enters u_j as
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const _Float16* __restri
         const float mvv[4] = {mv.x, mv.y, mv.z, mv.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = (live && valid_own) ? exp2f(lg[mb][i] - m_new) : 0.f;
+          const float p = (live && valid_own) ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;
           psum += p;
           msum = fmaf(p, mvv[i], msum);
           wv[hh][i] = p * svv[i];
@@ -417,16 +428,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const _Float16* __restri
     __builtin_amdgcn_wave_barrier();
   };
 
-  Pair<KB, VB, P> bufA, bufB;
-  if (g_begin < g_end) {
-    const uint8_t* rec[P];
-    recs(g_begin, rec);
-    load_pair<KB, VB, P>(bufA, rec, lane);
-  }
-  for (int gi = g_begin; gi < g_end; gi += 2) {
-    step(bufA, bufB, gi);
-    if (gi + 1 < g_end) step(bufB, bufA, gi + 1);
-  }
+  for (int gi = g_begin; gi < g_end; ++gi) step(gi);
 
   // ---- merge the 4 waves x P streams of each head, write one partial per head ----------
   const float l_col = rows_sum4(l_part);
@@ -456,7 +458,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const _Float16* __restri
 #pragma unroll
         for (int e = 0; e < P; ++e) {
           const float* row = lds + (w * 16 + e * G + g) * MRG;
-          const float f = exp2f(row[0] - M);
+          const float f = __builtin_amdgcn_exp2f(row[0] - M);
           L = fmaf(row[1], f, L);
           A = fmaf(row[2 + j], f, A);
         }
@@ -521,13 +523,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
     if (M != -INFINITY) {
       for (int k = r; k < n_splits; k += 32) {
         const float mk = part[k * kPartialFloats];
-        if (mk != -INFINITY) L = fmaf(part[k * kPartialFloats + 1], exp2f(mk - M), L);
+        if (mk != -INFINITY) L = fmaf(part[k * kPartialFloats + 1], __builtin_amdgcn_exp2f(mk - M), L);
       }
-      for (int t = r; t < nt; t += 32) L += exp2f(lg[g][t] - M);
+      for (int t = r; t < nt; t += 32) L += __builtin_amdgcn_exp2f(lg[g][t] - M);
       for (int k = 0; k < n_splits; ++k) {
         const float mk = part[k * kPartialFloats];
         if (mk == -INFINITY) continue;
-        const float f = exp2f(mk - M);
+        const float f = __builtin_amdgcn_exp2f(mk - M);
         const float4 a = *reinterpret_cast<const float4*>(part + k * kPartialFloats + 2 + 4 * r);
         ar[0] = fmaf(a.x, f, ar[0]);
         ar[1] = fmaf(a.y, f, ar[1]);
@@ -535,7 +537,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
         ar[3] = fmaf(a.w, f, ar[3]);
       }
       for (int t = 0; t < nt; ++t) {
-        const float f = exp2f(lg[g][t] - M);
+        const float f = __builtin_amdgcn_exp2f(lg[g][t] - M);
         const _Float16* vr = tail_v + tail_base + t * kCh + 4 * r;
 #pragma unroll
         for (int c = 0; c < 4; ++c) aw[c] = fmaf(f, static_cast<float>(vr[c]), aw[c]);

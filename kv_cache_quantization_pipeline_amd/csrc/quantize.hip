@@ -34,52 +34,6 @@ struct TileRegs {
   f32x4 y[4][8];
 };
 
-template <int BITS>
-__device__ __forceinline__ void store_k_unit(uint8_t* p, const uint32_t (&q)[8]) {
-  if constexpr (BITS == 4) {
-    uint32_t u = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u |= q[e] << (4 * e);
-    *reinterpret_cast<uint32_t*>(p) = u;
-  } else if constexpr (BITS == 8) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lo |= q[e] << (8 * e);
-      hi |= q[e + 4] << (8 * e);
-    }
-    *reinterpret_cast<u32x2*>(p) = u32x2{lo, hi};
-  } else {  // 2 bits
-    uint32_t u = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) u |= q[e] << (2 * e);
-    *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(u);
-  }
-}
-
-template <int BITS>
-__device__ __forceinline__ void store_v_unit(uint8_t* p, const uint32_t (&q)[16]) {
-  if constexpr (BITS == 2) {
-    uint32_t u = 0;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) u |= q[c] << (2 * c);
-    *reinterpret_cast<uint32_t*>(p) = u;
-  } else if constexpr (BITS == 4) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      lo |= q[c] << (4 * c);
-      hi |= q[c + 8] << (4 * c);
-    }
-    *reinterpret_cast<u32x2*>(p) = u32x2{lo, hi};
-  } else {  // 8 bits
-    uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int c = 0; c < 16; ++c) w[c >> 2] |= q[c] << (8 * (c & 3));
-    *reinterpret_cast<u32x4*>(p) = u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-
 // All-gather over the 4 lane rows of a value held in the reduce-scatter layout
 // (row r holds slot order[r] with order = {0, 2, 1, 3}): returns v[k] = slot k.
 __device__ __forceinline__ void rows_allgather4(float s, float (&v)[4]) {
@@ -95,100 +49,115 @@ __device__ __forceinline__ void rows_allgather4(float s, float (&v)[4]) {
   v[3] = g;
 }
 
-// Codes and stores for one tile half once the channel sums S~_j are known.
+// Codes and stores for one tile half once the channel sums S~_j are known.  R holds Ytilde on
+// entry and W = Ytilde exp(-v~) (= Y exp(-v)) afterwards.
 template <int BITS>
-__device__ __forceinline__ void quantize_store(const TileRegs& R, const float (&sfin)[8], uint8_t* rec, int code_off,
+__device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[8], uint8_t* rec, int code_off,
                                                int scale_off, bool is_v, int half, int gr, int nl) {
   constexpr int qmax = (1 << BITS) - 1;
-  float bsc[8];
+  // fma(d, inv, 1.5*2^23) rounds d*inv to the nearest integer (ties to even) in one step and
+  // leaves that integer in the low mantissa bits (d*inv is in [0, qmax]).
+  constexpr float kRound = 12582912.0f;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) bsc[nb] = __builtin_amdgcn_rsqf(sfin[nb]);  // exp(-v~_j)
+  for (int nb = 0; nb < 8; ++nb) {
+    const float b = __builtin_amdgcn_rsqf(sfin[nb]);  // exp(-v~_j)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) R.y[mb][nb] *= b;
+  }
 
-  float inv[4][4], bias[4][4], sp[4][4], mp[4][4];
+  float inv[4][4], mnv[4][4];
+  float* sc = reinterpret_cast<float*>(rec + scale_off);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
+    float sp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float mn = R.y[mb][0][i] * bsc[0], mx = mn;
+      float mn = R.y[mb][0][i], mx = mn;
 #pragma unroll
       for (int nb = 1; nb < 8; ++nb) {
-        const float w = R.y[mb][nb][i] * bsc[nb];
-        mn = fminf(mn, w);
-        mx = fmaxf(mx, w);
+        mn = fminf(mn, R.y[mb][nb][i]);
+        mx = fmaxf(mx, R.y[mb][nb][i]);
       }
       mn = row_min16(mn);
       mx = row_max16(mx);
       const float range = mx - mn;
-      sp[mb][i] = range * (1.0f / qmax);
-      mp[mb][i] = mn;
-      const float iv = range > 0.f ? qmax * fast_rcp(range) : 0.f;
-      inv[mb][i] = iv;
-      bias[mb][i] = -mn * iv;
+      sp[i] = range * (1.0f / qmax);
+      mnv[mb][i] = mn;
+      inv[mb][i] = range > 0.f ? qmax * fast_rcp(range) : 0.f;
     }
-
-  auto code = [&](int mb, int nb, int i) -> uint32_t {
-    const float w = R.y[mb][nb][i] * bsc[nb];
-    const float t = __builtin_rintf(fmaf(w, inv[mb][i], bias[mb][i]));
-    const uint32_t c = static_cast<uint32_t>(fmaxf(t, 0.f));
-    return c > qmax ? qmax : c;
-  };
-
-  if (!is_v) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t q[8];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) q[nb] = code(mb, nb, i);
-        const int t = 64 * half + 16 * mb + 4 * gr + i;
-        store_k_unit<BITS>(rec + code_off + t * 16 * BITS + nl * BITS, q);
-      }
-  } else {
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      uint32_t q[16];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) q[4 * mb + i] = code(mb, nb, i);
-      store_v_unit<BITS>(rec + code_off + ((nb * 4 + gr) * 16 + nl) * 4 * BITS + half * 2 * BITS, q);
-    }
-  }
-
-  float* sc = reinterpret_cast<float*>(rec + scale_off);
-  if (half == 0 && gr == 0) {
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) sc[16 * nb + nl] = __builtin_sqrtf(sfin[nb] * (1.0f / 128.0f));
-  }
-  if (nl < 4) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const float s = nl == 0 ? sp[mb][0] : nl == 1 ? sp[mb][1] : nl == 2 ? sp[mb][2] : sp[mb][3];
-      const float m = nl == 0 ? mp[mb][0] : nl == 1 ? mp[mb][1] : nl == 2 ? mp[mb][2] : mp[mb][3];
+    if (nl < 4) {
+      const float s = nl == 0 ? sp[0] : nl == 1 ? sp[1] : nl == 2 ? sp[2] : sp[3];
+      const float m = nl == 0 ? mnv[mb][0] : nl == 1 ? mnv[mb][1] : nl == 2 ? mnv[mb][2] : mnv[mb][3];
       const int t = 64 * half + 16 * mb + 4 * gr + nl;
       sc[128 + t] = s;
       sc[256 + t] = m;
     }
   }
+  if (half == 0 && gr == 0) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) sc[16 * nb + nl] = __builtin_sqrtf(sfin[nb] * (1.0f / 128.0f));
+  }
+
+  auto code = [&](int mb, int nb, int i) -> uint32_t {
+    const float f = fmaf(R.y[mb][nb][i] - mnv[mb][i], inv[mb][i], kRound);
+    return as_u(f) & static_cast<uint32_t>(qmax);
+  };
+
+  if (!is_v) {
+    // K unit of token t, lane nl: channels nl + 16e at bit BITS*e
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 64 * half + 16 * mb + 4 * gr + i;
+        uint8_t* p = rec + code_off + t * 16 * BITS + nl * BITS;
+        if constexpr (BITS == 8) {
+          uint32_t lo = 0, hi = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo |= code(mb, e, i) << (8 * e);
+            hi |= code(mb, e + 4, i) << (8 * e);
+          }
+          *reinterpret_cast<u32x2*>(p) = u32x2{lo, hi};
+        } else {
+          uint32_t u = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) u |= code(mb, e, i) << (BITS * e);
+          if constexpr (BITS == 4)
+            *reinterpret_cast<uint32_t*>(p) = u;
+          else
+            *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(u);
+        }
+      }
+  } else {
+    // V unit (nb, gr, nl, half): tokens (mb, i) at bit BITS*(4mb + i)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      uint8_t* p = rec + code_off + ((nb * 4 + gr) * 16 + nl) * 4 * BITS + half * 2 * BITS;
+      constexpr int W = BITS / 2;  // 32-bit words per unit
+      uint32_t u[W];
+#pragma unroll
+      for (int k = 0; k < W; ++k) u[k] = 0;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 4 * mb + i;
+          u[(c * BITS) / 32] |= code(mb, nb, i) << ((c * BITS) % 32);
+        }
+      if constexpr (W == 1)
+        *reinterpret_cast<uint32_t*>(p) = u[0];
+      else if constexpr (W == 2)
+        *reinterpret_cast<u32x2*>(p) = u32x2{u[0], u[1]};
+      else
+        *reinterpret_cast<u32x4*>(p) = u32x4{u[0], u[1], u[2], u[3]};
+    }
+  }
 }
 
-}  // namespace
-
-// Quantise the tile half owned by this pair of waves and write its part of the
-// record.  x: token 0, channel 0; row t at x + t*row_stride (halves); when
-// last_row is non-null token 127 is read from there.  xch: LDS [2][4][64].
-__device__ void quantize_tile_half(const _Float16* __restrict__ x, int64_t row_stride,
-                                   const _Float16* __restrict__ last_row, uint8_t* __restrict__ rec, int kb,
-                                   int vb, int iters, float2 (*xch)[4][64]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int half = wave & 1;
-  const bool is_v = wave >= 2;
-  const int nl = lane & 15, gr = lane >> 4;
-
-  // 1. MFMA A operands: token 16*mb + nl of this wave, channels 32*kb + 8*gr + s.
-  f16x8 xa[4][4];
+// MFMA A operands of this wave's 64 tokens: token 16*mb + nl, channels 32*k4 + 8*gr + s.
+__device__ __forceinline__ void load_x(f16x8 (&xa)[4][4], const _Float16* __restrict__ x, int64_t row_stride,
+                                       const _Float16* __restrict__ last_row, int half, int gr, int nl) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int t = 64 * half + 16 * mb + nl;
@@ -196,10 +165,12 @@ __device__ void quantize_tile_half(const _Float16* __restrict__ x, int64_t row_s
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) xa[mb][k4] = *reinterpret_cast<const f16x8*>(row + 32 * k4 + 8 * gr);
   }
+}
 
-  // 2. B operands of H_128: entry (k, n) = (-1)^popcount(k & n) with k = 32*kb + 8*gr + s and
-  //    n = 16*nb + nl splits into a lane pattern (s, gr bit 0, nl), a lane sign for odd nb
-  //    (gr bit 1) and a sign uniform over the wave (popcount(kb & (nb >> 1))).
+// Ytilde = X H_128 on the matrix cores.  Entry (k, n) of H is (-1)^popcount(k & n) with
+// k = 32*k4 + 8*gr + s and n = 16*nb + nl; it splits into a lane pattern (s, gr bit 0, nl),
+// a lane sign for odd nb (gr bit 1) and a sign uniform over the wave (popcount(k4 & (nb >> 1))).
+__device__ __forceinline__ void rotate(const f16x8 (&xa)[4][4], TileRegs& R, int gr, int nl) {
   f16x8 P0, N0, P1, N1;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -209,8 +180,6 @@ __device__ void quantize_tile_half(const _Float16* __restrict__ x, int64_t row_s
   N0 = -P0;
   P1 = (gr >> 1) ? N0 : P0;
   N1 = -P1;
-
-  TileRegs R;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -224,16 +193,39 @@ __device__ void quantize_tile_half(const _Float16* __restrict__ x, int64_t row_s
       }
       R.y[mb][nb] = c;
     }
+}
 
-  // 3. Sinkhorn.  w[mb][i] = exp(-2u_t)/128 (token weights), e[nb] = exp(-2v~_j).
-  float A[4][8][4];
+}  // namespace
+
+// Quantise the tile half owned by this pair of waves and write its part of the
+// record.  x: token 0, channel 0; row t at x + t*row_stride (halves); when
+// last_row is non-null token 127 is read from there.  xch: LDS [2][4][64].
+template <int KB, int VB>
+__device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ x, int64_t row_stride,
+                                                   const _Float16* __restrict__ last_row, uint8_t* __restrict__ rec,
+                                                   int iters, float2 (*xch)[4][64]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = wave & 1;
+  const bool is_v = wave >= 2;
+  const int nl = lane & 15, gr = lane >> 4;
+
+  // 1-2. load the tile half and rotate it on the matrix cores; only A = Ytilde^2 is kept through
+  //      the Sinkhorn iterations (Ytilde is recomputed afterwards, so a wave needs 128 values per lane
+  //      and two waves fit on each SIMD)
+  TileRegs R;
+  {
+    f16x8 xa[4][4];
+    load_x(xa, x, row_stride, last_row, half, gr, nl);
+    rotate(xa, R, gr, nl);
+  }
+  auto& A = R.y;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) A[mb][nb][i] = R.y[mb][nb][i] * R.y[mb][nb][i];
+    for (int nb = 0; nb < 8; ++nb) A[mb][nb] *= A[mb][nb];
 
+  // 3. Sinkhorn.  w[mb][i] = exp(-2u_t)/128 (token weights), e[nb] = exp(-2v~_j).
   float w[4][4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -299,23 +291,27 @@ __device__ void quantize_tile_half(const _Float16* __restrict__ x, int64_t row_s
       }
   }
 
+  // 4. Ytilde again (the tile is still in L2), then codes, scales, stores
+  {
+    f16x8 xa[4][4];
+    load_x(xa, x, row_stride, last_row, half, gr, nl);
+    rotate(xa, R, gr, nl);
+  }
   // 4. codes, scales, stores
-  const int bits = is_v ? vb : kb;
-  const int code_off = is_v ? k_code_bytes(kb) : 0;
-  const int scale_off = scale_offset(kb, vb) + (is_v ? 3 * 512 : 0);
-  if (bits == 4)
-    quantize_store<4>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl);
-  else if (bits == 2)
-    quantize_store<2>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl);
+  const int code_off = is_v ? k_code_bytes(KB) : 0;
+  const int scale_off = scale_offset(KB, VB) + (is_v ? 3 * 512 : 0);
+  if (is_v)
+    quantize_store<VB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl);
   else
-    quantize_store<8>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl);
+    quantize_store<KB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl);
 }
 
-__global__ __launch_bounds__(256, 1) void quantize_tiles_kernel(const _Float16* __restrict__ k,
+template <int KB, int VB>
+__global__ __launch_bounds__(256, 2) void quantize_tiles_kernel(const _Float16* __restrict__ k,
                                                                 const _Float16* __restrict__ v,
                                                                 const int32_t* __restrict__ dst_pages,
                                                                 uint8_t* __restrict__ cache, int64_t page_stride,
-                                                                int num_kv_heads, int kb, int vb, int iters) {
+                                                                int num_kv_heads, int iters) {
   __shared__ float2 xch[2][4][64];
   const int tile = blockIdx.x / num_kv_heads;
   const int h = blockIdx.x - tile * num_kv_heads;
@@ -323,20 +319,21 @@ __global__ __launch_bounds__(256, 1) void quantize_tiles_kernel(const _Float16* 
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * kCh;
   const _Float16* src = (is_v ? v : k) + (static_cast<int64_t>(tile) * kTok * num_kv_heads + h) * kCh;
   uint8_t* rec = cache + static_cast<int64_t>(dst_pages[tile]) * page_stride +
-                 static_cast<int64_t>(h) * record_bytes(kb, vb);
-  quantize_tile_half(src, row_stride, nullptr, rec, kb, vb, iters, xch);
+                 static_cast<int64_t>(h) * record_bytes(KB, VB);
+  quantize_tile_half<KB, VB>(src, row_stride, nullptr, rec, iters, xch);
 }
 
 // Token append: one workgroup per (sequence, kv head).  Writes the new token into
 // the fp16 tail at len % 128 and, when that fills the tile, quantises the tail
 // (token 127 read from the new token itself) into page_table[s][len / 128].
-__global__ __launch_bounds__(256, 1) void append_kernel(const _Float16* __restrict__ k_new,
+template <int KB, int VB>
+__global__ __launch_bounds__(256, 2) void append_kernel(const _Float16* __restrict__ k_new,
                                                         const _Float16* __restrict__ v_new,
                                                         const int32_t* __restrict__ seq_lens,
                                                         _Float16* __restrict__ tail_k, _Float16* __restrict__ tail_v,
                                                         const int32_t* __restrict__ page_table, int max_pages,
                                                         uint8_t* __restrict__ cache, int64_t page_stride,
-                                                        int num_kv_heads, int kb, int vb, int iters) {
+                                                        int num_kv_heads, int iters) {
   __shared__ float2 xch[2][4][64];
   const int sh = blockIdx.x;
   const int s = sh / num_kv_heads;
@@ -356,8 +353,8 @@ __global__ __launch_bounds__(256, 1) void append_kernel(const _Float16* __restri
     const _Float16* x = (is_v ? tail_v : tail_k) + tail_base;
     const _Float16* last = (is_v ? v_new : k_new) + static_cast<int64_t>(sh) * kCh;
     const int page = page_table[static_cast<int64_t>(s) * max_pages + (len >> 7)];
-    uint8_t* rec = cache + static_cast<int64_t>(page) * page_stride + static_cast<int64_t>(h) * record_bytes(kb, vb);
-    quantize_tile_half(x, kCh, last, rec, kb, vb, iters, xch);
+    uint8_t* rec = cache + static_cast<int64_t>(page) * page_stride + static_cast<int64_t>(h) * record_bytes(KB, VB);
+    quantize_tile_half<KB, VB>(x, kCh, last, rec, iters, xch);
   }
 }
 
@@ -366,13 +363,22 @@ __global__ void seq_len_increment_kernel(int32_t* __restrict__ seq_lens, int n) 
   if (i < n) seq_lens[i] += 1;
 }
 
+// (kb, vb) -> the kernel instantiation for that format
+#define KVARN_FOR_EACH_FORMAT(X) X(2, 2) X(2, 4) X(2, 8) X(4, 2) X(4, 4) X(4, 8) X(8, 2) X(8, 4) X(8, 8)
+
 hipError_t launch_quantize_tiles(const _Float16* k, const _Float16* v, const int32_t* dst_pages, uint8_t* cache,
                                  int64_t page_stride, int num_tiles, int num_kv_heads, int kb, int vb, int iters,
                                  hipStream_t stream) {
   if (num_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_tiles_kernel, dim3(num_tiles * num_kv_heads), dim3(256), 0, stream, k, v, dst_pages,
-                     cache, page_stride, num_kv_heads, kb, vb, iters);
-  return hipGetLastError();
+#define KVARN_Q(KB_, VB_)                                                                                          \
+  if (kb == KB_ && vb == VB_) {                                                                                    \
+    hipLaunchKernelGGL((quantize_tiles_kernel<KB_, VB_>), dim3(num_tiles * num_kv_heads), dim3(256), 0, stream, k, \
+                       v, dst_pages, cache, page_stride, num_kv_heads, iters);                                     \
+    return hipGetLastError();                                                                                      \
+  }
+  KVARN_FOR_EACH_FORMAT(KVARN_Q)
+#undef KVARN_Q
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_append(const _Float16* k_new, const _Float16* v_new, int32_t* seq_lens, _Float16* tail_k,
@@ -380,9 +386,16 @@ hipError_t launch_append(const _Float16* k_new, const _Float16* v_new, int32_t* 
                          int64_t page_stride, int num_seqs, int num_kv_heads, int kb, int vb, int iters,
                          hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
-  hipLaunchKernelGGL(append_kernel, dim3(num_seqs * num_kv_heads), dim3(256), 0, stream, k_new, v_new, seq_lens,
-                     tail_k, tail_v, page_table, max_pages, cache, page_stride, num_kv_heads, kb, vb, iters);
-  hipError_t e = hipGetLastError();
+  hipError_t e = hipErrorInvalidValue;
+#define KVARN_A(KB_, VB_)                                                                                       \
+  if (kb == KB_ && vb == VB_) {                                                                                 \
+    hipLaunchKernelGGL((append_kernel<KB_, VB_>), dim3(num_seqs * num_kv_heads), dim3(256), 0, stream, k_new,   \
+                       v_new, seq_lens, tail_k, tail_v, page_table, max_pages, cache, page_stride, num_kv_heads, \
+                       iters);                                                                                  \
+    e = hipGetLastError();                                                                                      \
+  }
+  KVARN_FOR_EACH_FORMAT(KVARN_A)
+#undef KVARN_A
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(seq_len_increment_kernel, dim3((num_seqs + 255) / 256), dim3(256), 0, stream, seq_lens, num_seqs);
   return hipGetLastError();
