@@ -28,6 +28,14 @@ namespace kvarn {
 
 namespace {
 
+// Per-wave LDS scratch for transposing per-token values across the 16 lanes of a lane row:
+// tb[lane][*] holds a lane's per-token partials, wb[row][*] the per-token results broadcast back.
+constexpr int kTbStride = 34;  // 32 values + 2 padding floats per lane (8-byte aligned rows)
+struct WaveLds {
+  float tb[64][kTbStride];
+  float wb[4][32];
+};
+
 // C-layout of v_mfma_f32_16x16x32_f16 for this wave's 64 tokens x 128 channels:
 // y[mb][nb][i] = Ytilde[t = 64*half + 16*mb + 4*gr + i][j = 16*nb + nl].
 struct TileRegs {
@@ -53,7 +61,7 @@ __device__ __forceinline__ void rows_allgather4(float s, float (&v)[4]) {
 // entry and W = Ytilde exp(-v~) (= Y exp(-v)) afterwards.
 template <int BITS>
 __device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[8], uint8_t* rec, int code_off,
-                                               int scale_off, bool is_v, int half, int gr, int nl) {
+                                               int scale_off, bool is_v, int half, int gr, int nl, WaveLds& L) {
   constexpr int qmax = (1 << BITS) - 1;
   // fma(d, inv, 1.5*2^23) rounds d*inv to the nearest integer (ties to even) in one step and
   // leaves that integer in the low mantissa bits (d*inv is in [0, qmax]).
@@ -65,11 +73,12 @@ __device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[
     for (int mb = 0; mb < 4; ++mb) R.y[mb][nb] *= b;
   }
 
-  float inv[4][4], mnv[4][4];
   float* sc = reinterpret_cast<float*>(rec + scale_off);
+  const int lane = 16 * gr + nl;
+  // per-token min / max: this lane's 8 channels, then the 16 lanes of the row through an LDS
+  // transpose (lane nl of a row reduces token k = nl = 4*mb + i of that row)
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    float sp[4];
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float mn = R.y[mb][0][i], mx = mn;
@@ -78,21 +87,41 @@ __device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[
         mn = fminf(mn, R.y[mb][nb][i]);
         mx = fmaxf(mx, R.y[mb][nb][i]);
       }
-      mn = row_min16(mn);
-      mx = row_max16(mx);
-      const float range = mx - mn;
-      sp[i] = range * (1.0f / qmax);
-      mnv[mb][i] = mn;
-      inv[mb][i] = range > 0.f ? qmax * fast_rcp(range) : 0.f;
+      *reinterpret_cast<float2*>(&L.tb[lane][2 * (4 * mb + i)]) = make_float2(mn, mx);
     }
-    if (nl < 4) {
-      const float s = nl == 0 ? sp[0] : nl == 1 ? sp[1] : nl == 2 ? sp[2] : sp[3];
-      const float m = nl == 0 ? mnv[mb][0] : nl == 1 ? mnv[mb][1] : nl == 2 ? mnv[mb][2] : mnv[mb][3];
-      const int t = 64 * half + 16 * mb + 4 * gr + nl;
-      sc[128 + t] = s;
-      sc[256 + t] = m;
+  __builtin_amdgcn_wave_barrier();
+  float mn_own, mx_own;
+  {
+    const float2 v0 = *reinterpret_cast<const float2*>(&L.tb[16 * gr][2 * nl]);
+    mn_own = v0.x;
+    mx_own = v0.y;
+#pragma unroll
+    for (int l = 1; l < 16; ++l) {
+      const float2 v = *reinterpret_cast<const float2*>(&L.tb[16 * gr + l][2 * nl]);
+      mn_own = fminf(mn_own, v.x);
+      mx_own = fmaxf(mx_own, v.y);
     }
   }
+  {
+    const float range = mx_own - mn_own;
+    const float inv_own = range > 0.f ? qmax * fast_rcp(range) : 0.f;
+    const int t = 64 * half + 16 * (nl >> 2) + 4 * gr + (nl & 3);
+    sc[128 + t] = range * (1.0f / qmax);
+    sc[256 + t] = mn_own;
+    *reinterpret_cast<float2*>(&L.wb[gr][2 * nl]) = make_float2(mn_own, inv_own);
+  }
+  __builtin_amdgcn_wave_barrier();
+  float inv[4][4], mnv[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const float4 v = *reinterpret_cast<const float4*>(&L.wb[gr][8 * mb + 4 * ii]);
+      mnv[mb][2 * ii] = v.x;
+      inv[mb][2 * ii] = v.y;
+      mnv[mb][2 * ii + 1] = v.z;
+      inv[mb][2 * ii + 1] = v.w;
+    }
   if (half == 0 && gr == 0) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) sc[16 * nb + nl] = __builtin_sqrtf(sfin[nb] * (1.0f / 128.0f));
@@ -203,12 +232,16 @@ __device__ __forceinline__ void rotate(const f16x8 (&xa)[4][4], TileRegs& R, int
 template <int KB, int VB>
 __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ x, int64_t row_stride,
                                                    const _Float16* __restrict__ last_row, uint8_t* __restrict__ rec,
-                                                   int iters, float2 (*xch)[4][64]) {
+                                                   int iters, float2 (*xch)[4][64], WaveLds* wlds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = wave & 1;
   const bool is_v = wave >= 2;
   const int nl = lane & 15, gr = lane >> 4;
+  WaveLds& L = wlds[wave];
+  // Every row / column sum starts at kEps: a sum over an all-zero row or column stays positive, its
+  // reciprocal only ever multiplies zeros, and no zero test is needed in the iterations.
+  constexpr float kEps = 1e-30f;
 
   // 1-2. load the tile half and rotate it on the matrix cores; only A = Ytilde^2 is kept through
   //      the Sinkhorn iterations (Ytilde is recomputed afterwards, so a wave needs 128 values per lane
@@ -255,10 +288,12 @@ __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ 
     buf[wave][lane] = make_float2(s0, s1);
     __syncthreads();
     const float2 o = buf[wave ^ 1][lane];
+    // own + partner is commutative, so both waves of the pair hold identical sums
     s0 += o.x;
     s1 += o.y;
     const bool last = (it == iters - 1);
     if (last) {
+      // an all-zero channel (sum exactly 0) keeps log-scale 0: stored c_j = 1 <=> S~_j = 128
       float v[4];
       rows_allgather4(s0 > 0.f ? s0 : 128.0f, v);
 #pragma unroll
@@ -268,27 +303,49 @@ __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ 
       for (int k = 0; k < 4; ++k) sfin[4 + k] = v[k];
       break;
     }
+    s0 += kEps;
+    s1 += kEps;
     float e[8];
     {
       float v[4];
-      rows_allgather4(s0 > 0.f ? fast_rcp(s0) : 1.0f / 128.0f, v);
+      rows_allgather4(fast_rcp(s0), v);
 #pragma unroll
       for (int k = 0; k < 4; ++k) e[k] = v[k];
-      rows_allgather4(s1 > 0.f ? fast_rcp(s1) : 1.0f / 128.0f, v);
+      rows_allgather4(fast_rcp(s1), v);
 #pragma unroll
       for (int k = 0; k < 4; ++k) e[4 + k] = v[k];
     }
-    // token pass: R_t = sum_j A_tj e_j over the 16 lanes of the row
+    // token pass: R_t = sum_j A_tj e_j.  Each lane forms 16 partials (its 8 channels); the 16 lanes
+    // of a row are summed through an LDS transpose, lane nl owning token 4*mb + i = nl, whose
+    // reciprocal is broadcast back to the row.
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float acc = 0.f;
+      for (int ii = 0; ii < 2; ++ii) {
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) acc = fmaf(A[mb][nb][i], e[nb], acc);
-        acc = row_sum16(acc);
-        w[mb][i] = acc > 0.f ? fast_rcp(acc) : 1.0f / 128.0f;
+        for (int nb = 0; nb < 8; ++nb) {
+          a0 = fmaf(A[mb][nb][2 * ii], e[nb], a0);
+          a1 = fmaf(A[mb][nb][2 * ii + 1], e[nb], a1);
+        }
+        *reinterpret_cast<float2*>(&L.tb[lane][4 * mb + 2 * ii]) = make_float2(a0, a1);
       }
+    __builtin_amdgcn_wave_barrier();
+    {
+      float r = kEps;
+#pragma unroll
+      for (int l = 0; l < 16; ++l) r += L.tb[16 * gr + l][nl];
+      L.wb[gr][nl] = fast_rcp(r);
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const float4 v = *reinterpret_cast<const float4*>(&L.wb[gr][4 * mb]);
+      w[mb][0] = v.x;
+      w[mb][1] = v.y;
+      w[mb][2] = v.z;
+      w[mb][3] = v.w;
+    }
   }
 
   // 4. Ytilde again (the tile is still in L2), then codes, scales, stores
@@ -301,9 +358,9 @@ __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ 
   const int code_off = is_v ? k_code_bytes(KB) : 0;
   const int scale_off = scale_offset(KB, VB) + (is_v ? 3 * 512 : 0);
   if (is_v)
-    quantize_store<VB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl);
+    quantize_store<VB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl, L);
   else
-    quantize_store<KB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl);
+    quantize_store<KB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl, L);
 }
 
 template <int KB, int VB>
@@ -313,6 +370,7 @@ __global__ __launch_bounds__(256, 2) void quantize_tiles_kernel(const _Float16* 
                                                                 uint8_t* __restrict__ cache, int64_t page_stride,
                                                                 int num_kv_heads, int iters) {
   __shared__ float2 xch[2][4][64];
+  __shared__ WaveLds wlds[4];
   const int tile = blockIdx.x / num_kv_heads;
   const int h = blockIdx.x - tile * num_kv_heads;
   const bool is_v = (threadIdx.x >> 6) >= 2;
@@ -320,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void quantize_tiles_kernel(const _Float16* 
   const _Float16* src = (is_v ? v : k) + (static_cast<int64_t>(tile) * kTok * num_kv_heads + h) * kCh;
   uint8_t* rec = cache + static_cast<int64_t>(dst_pages[tile]) * page_stride +
                  static_cast<int64_t>(h) * record_bytes(KB, VB);
-  quantize_tile_half<KB, VB>(src, row_stride, nullptr, rec, iters, xch);
+  quantize_tile_half<KB, VB>(src, row_stride, nullptr, rec, iters, xch, wlds);
 }
 
 // Token append: one workgroup per (sequence, kv head).  Writes the new token into
@@ -335,6 +393,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(const _Float16* __restri
                                                         uint8_t* __restrict__ cache, int64_t page_stride,
                                                         int num_kv_heads, int iters) {
   __shared__ float2 xch[2][4][64];
+  __shared__ WaveLds wlds[4];
   const int sh = blockIdx.x;
   const int s = sh / num_kv_heads;
   const int h = sh - s * num_kv_heads;
@@ -354,7 +413,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(const _Float16* __restri
     const _Float16* last = (is_v ? v_new : k_new) + static_cast<int64_t>(sh) * kCh;
     const int page = page_table[static_cast<int64_t>(s) * max_pages + (len >> 7)];
     uint8_t* rec = cache + static_cast<int64_t>(page) * page_stride + static_cast<int64_t>(h) * record_bytes(KB, VB);
-    quantize_tile_half<KB, VB>(x, kCh, last, rec, iters, xch);
+    quantize_tile_half<KB, VB>(x, kCh, last, rec, iters, xch, wlds);
   }
 }
 
