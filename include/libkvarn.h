@@ -80,7 +80,8 @@ kvarn_status kvarn_format_check(const kvarn_format* f);
 size_t kvarn_record_bytes(const kvarn_format* f);
 
 /* Workspace bytes kvarn_decode_attention needs for these sizes (split-K partial results:
- * per (sequence, query head, split) a running max, a running sum and 128 accumulators). */
+ * per (sequence, query head, split) a running max, a running sum, 2 pad floats and 128
+ * accumulators, 528 bytes). */
 size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t max_pages_per_seq);
 

@@ -199,7 +199,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   const int s = sh / num_kv_heads;
   const int h = sh - s * num_kv_heads;
   const int sp = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, gr = lane >> 4;
 
   const int len = seq_lens[s];
@@ -252,26 +253,34 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   const int gpw = groups_per_split / 4;
   const int g_begin = sp * groups_per_split + wave * gpw;
   const int g_end = min(g_begin + gpw, n_groups);
-  float* sb = lds + wave * (P * SC);
+  float* const sb = lds + wave * (P * SC);
   const int64_t pt_row = static_cast<int64_t>(s) * max_pages;
   const int64_t head_off = static_cast<int64_t>(h) * R;
 
-  auto recs = [&](int gi, const uint8_t* (&rec)[P]) {
+  // Physical page ids of a group: a vector load (lane e < P holds page e of the group), issued one
+  // group ahead so that its latency hides behind the current group; read out with readlane.
+  auto page_ids = [&](int gi) -> int {
+    const int pg = gi * P + (lane & (P - 1));
+    return page_table[pt_row + (pg < n_pages ? pg : gi * P)];
+  };
+  auto recs = [&](int ids, const uint8_t* (&rec)[P]) {
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      const int pg = gi * P + e;
-      const int phys = page_table[pt_row + (pg < n_pages ? pg : gi * P)];
+      const int phys = __builtin_amdgcn_readlane(ids, e);
       rec[e] = cache + static_cast<int64_t>(phys) * page_stride + head_off;
     }
   };
 
-  // One group: load its codes and scales, stage the scales in LDS, compute.  Two waves share
-  // each SIMD, so one wave's loads overlap the other's arithmetic.
-  auto step = [&](int gi) {
+  // One group: load its K codes and scales, stage the scales in LDS, compute; the V codes are
+  // loaded once QK is done, into the registers of the consumed K codes (register budget of two
+  // waves per SIMD).  Two waves share each SIMD, so one wave's loads overlap the other's
+  // arithmetic.
+  auto step = [&](int gi, int ids, int& ids_next) {
     Pair<KB, VB, P> cur;
     const uint8_t* rec[P];
-    recs(gi, rec);
+    recs(ids, rec);
     load_pair<KB, VB, P>(cur, rec, lane);
+    if (gi + 1 < g_end) ids_next = page_ids(gi + 1);
 #pragma unroll
     for (int k = 0; k < 3 * P; ++k) reinterpret_cast<float4*>(sb)[lane + 64 * k] = cur.sc[k];
     __builtin_amdgcn_wave_barrier();
@@ -337,8 +346,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
       lg[mb][3] = fmaf(sk.w, dd[3], mk.w * sigma);
     }
 
-    // V codes are loaded only now, so that they are not live during QK (register budget of two
-    // waves per SIMD); the softmax below covers part of their latency
     __builtin_amdgcn_sched_barrier(0);
     load_pair_v<KB, VB, P>(cur, rec, lane);
 
@@ -428,7 +435,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
     __builtin_amdgcn_wave_barrier();
   };
 
-  for (int gi = g_begin; gi < g_end; ++gi) step(gi);
+  if (g_begin < g_end) {
+    int ids = page_ids(g_begin), ids_next = 0;
+    for (int gi = g_begin; gi < g_end; ++gi) {
+      step(gi, ids, ids_next);
+      ids = ids_next;
+    }
+  }
 
   // ---- merge the 4 waves x P streams of each head, write one partial per head ----------
   const float l_col = rows_sum4(l_part);
@@ -468,106 +481,125 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
       out[0] = M;
       out[1] = L;
     }
-    out[2 + j] = A;
+    out[4 + j] = A;
   }
 }
 
-// Merge the split-K partials with the fp16 tail, apply Hn once, normalise.
-// One workgroup per (sequence, kv head); 32 threads per query head, 4 channels each.
-template <int G>
+// Merge the split-K partials of one (sequence, query head) with its fp16 tail, apply Hn once,
+// normalise.  One workgroup of 256 threads per (sequence, query head); thread (cq, sl) =
+// (tid & 31, tid >> 5) sums channels 4cq .. 4cq+3 over the splits and tail tokens congruent to
+// sl mod 8, so that long contexts (many splits) are merged by all 256 threads.
 __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict__ q, const float* __restrict__ ws,
                                                      int n_splits, const int32_t* __restrict__ seq_lens,
                                                      const _Float16* __restrict__ tail_k,
                                                      const _Float16* __restrict__ tail_v, int num_q_heads,
-                                                     int num_kv_heads, float sm_log2e, _Float16* __restrict__ out) {
-  __shared__ float qs[G][kCh];
-  __shared__ float lg[G][kTok];
-  const int sh = blockIdx.x;
-  const int s = sh / num_kv_heads;
-  const int h = sh - s * num_kv_heads;
-  const int tid = threadIdx.x;
+                                                     int group_size, float sm_log2e, _Float16* __restrict__ out) {
+  __shared__ float qs[kCh];
+  __shared__ float lg[kTok];
+  __shared__ float red[8][2 * kCh];  // per token/split lane: rotated-domain and tail accumulators
+  __shared__ float wmax[4];
+  __shared__ float lsum[8];
+  const int sq = blockIdx.x;  // s * num_q_heads + query head
+  const int s = sq / num_q_heads;
+  const int hq = sq - s * num_q_heads;
+  const int num_kv_heads = num_q_heads / group_size;
+  const int hk = hq / group_size;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int len = seq_lens[s];
   const int nt = len & (kTok - 1);
-  const int64_t tail_base = static_cast<int64_t>(sh) * kTok * kCh;
+  const int64_t tail_base = (static_cast<int64_t>(s) * num_kv_heads + hk) * kTok * kCh;
+  const float* part = ws + static_cast<int64_t>(sq) * n_splits * kPartialFloats;
 
-  for (int idx = tid; idx < G * kCh; idx += 256)
-    qs[idx >> 7][idx & 127] =
-        static_cast<float>(q[(static_cast<int64_t>(s) * num_q_heads + h * G) * kCh + idx]) * sm_log2e;
+  if (tid < kCh) qs[tid] = static_cast<float>(q[static_cast<int64_t>(sq) * kCh + tid]) * sm_log2e;
   __syncthreads();
-  for (int idx = tid; idx < G * kTok; idx += 256) {
-    const int g = idx >> 7, t = idx & 127;
-    float d = -INFINITY;
-    if (t < nt) {
-      const _Float16* kr = tail_k + tail_base + t * kCh;
-      d = 0.f;
-      for (int j = 0; j < kCh; j += 8) {
-        const f16x8 kv = *reinterpret_cast<const f16x8*>(kr + j);
+  float mx = -INFINITY;
+  if (tid < nt) {
+    const _Float16* kr = tail_k + tail_base + static_cast<int64_t>(tid) * kCh;
+    float d = 0.f;
+    for (int j = 0; j < kCh; j += 8) {
+      const f16x8 kv = *reinterpret_cast<const f16x8*>(kr + j);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) d = fmaf(qs[g][j + c], static_cast<float>(kv[c]), d);
-      }
+      for (int c = 0; c < 8; ++c) d = fmaf(qs[j + c], static_cast<float>(kv[c]), d);
     }
-    lg[g][t] = d;
+    lg[tid] = d;
+    mx = d;
   }
+  for (int k = tid; k < n_splits; k += 256) mx = fmaxf(mx, part[k * kPartialFloats]);
+#pragma unroll
+  for (int b = 32; b >= 1; b >>= 1) mx = fmaxf(mx, __shfl_xor(mx, b));
+  if (lane == 0) wmax[wave] = mx;
   __syncthreads();
+  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 
-  const int r = tid & 31;
-  for (int g = tid >> 5; g < G; g += 8) {
-    const float* part = ws + (static_cast<int64_t>(s) * num_q_heads + h * G + g) * n_splits * kPartialFloats;
-    float M = -INFINITY;
-    for (int k = r; k < n_splits; k += 32) M = fmaxf(M, part[k * kPartialFloats]);
-    for (int t = r; t < nt; t += 32) M = fmaxf(M, lg[g][t]);
-#pragma unroll
-    for (int b = 16; b >= 1; b >>= 1) M = fmaxf(M, __shfl_xor(M, b, 32));
-    float L = 0.f;
-    float ar[4] = {0.f, 0.f, 0.f, 0.f}, aw[4] = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-      for (int k = r; k < n_splits; k += 32) {
-        const float mk = part[k * kPartialFloats];
-        if (mk != -INFINITY) L = fmaf(part[k * kPartialFloats + 1], __builtin_amdgcn_exp2f(mk - M), L);
-      }
-      for (int t = r; t < nt; t += 32) L += __builtin_amdgcn_exp2f(lg[g][t] - M);
-      for (int k = 0; k < n_splits; ++k) {
-        const float mk = part[k * kPartialFloats];
-        if (mk == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(mk - M);
-        const float4 a = *reinterpret_cast<const float4*>(part + k * kPartialFloats + 2 + 4 * r);
-        ar[0] = fmaf(a.x, f, ar[0]);
-        ar[1] = fmaf(a.y, f, ar[1]);
-        ar[2] = fmaf(a.z, f, ar[2]);
-        ar[3] = fmaf(a.w, f, ar[3]);
-      }
-      for (int t = 0; t < nt; ++t) {
-        const float f = __builtin_amdgcn_exp2f(lg[g][t] - M);
-        const _Float16* vr = tail_v + tail_base + t * kCh + 4 * r;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) aw[c] = fmaf(f, static_cast<float>(vr[c]), aw[c]);
-      }
+  const int cq = tid & 31, sl = tid >> 5;
+  float ar[4] = {0.f, 0.f, 0.f, 0.f}, aw[4] = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != -INFINITY) {
+    // an empty split holds (-inf, 0, 0...): its factor exp2(-inf) is 0
+#pragma unroll 4
+    for (int k = sl; k < n_splits; k += 8) {
+      const float* pk = part + k * kPartialFloats;
+      const float f = __builtin_amdgcn_exp2f(pk[0] - M);
+      L = fmaf(pk[1], f, L);
+      const float4 a = *reinterpret_cast<const float4*>(pk + 4 + 4 * cq);
+      ar[0] = fmaf(a.x, f, ar[0]);
+      ar[1] = fmaf(a.y, f, ar[1]);
+      ar[2] = fmaf(a.z, f, ar[2]);
+      ar[3] = fmaf(a.w, f, ar[3]);
     }
+    for (int t = sl; t < nt; t += 8) {
+      const float f = __builtin_amdgcn_exp2f(lg[t] - M);
+      L += f;
+      const _Float16* vr = tail_v + tail_base + static_cast<int64_t>(t) * kCh + 4 * cq;
 #pragma unroll
-    for (int b = 16; b >= 1; b >>= 1) L += __shfl_xor(L, b, 32);
-    // Hn over the 128 rotated-domain channels (4 per thread: 2 stages in registers, 5 across lanes)
-    {
-      const float a0 = ar[0] + ar[1], a1 = ar[0] - ar[1], a2 = ar[2] + ar[3], a3 = ar[2] - ar[3];
-      ar[0] = a0 + a2;
-      ar[1] = a1 + a3;
-      ar[2] = a0 - a2;
-      ar[3] = a1 - a3;
-#pragma unroll
-      for (int b = 0; b < 5; ++b) {
-        const bool upper = (r >> b) & 1;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float o = __shfl_xor(ar[c], 1 << b, 32);
-          ar[c] = upper ? o - ar[c] : ar[c] + o;
-        }
-      }
+      for (int c = 0; c < 4; ++c) aw[c] = fmaf(f, static_cast<float>(vr[c]), aw[c]);
     }
-    const float inv_l = L > 0.f ? 1.0f / L : 0.f;
-    constexpr float kInvSqrt128 = 0.08838834764831845f;
-    _Float16* o = out + (static_cast<int64_t>(s) * num_q_heads + h * G + g) * kCh + 4 * r;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = static_cast<_Float16>((ar[c] * kInvSqrt128 + aw[c]) * inv_l);
   }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    red[sl][4 * cq + c] = ar[c];
+    red[sl][kCh + 4 * cq + c] = aw[c];
+  }
+  if (cq == 0) lsum[sl] = L;
+  __syncthreads();
+  if (wave != 0) return;
+
+  // wave 0: channels 2*lane, 2*lane + 1; Hn over the rotated-domain sum (1 stage in registers,
+  // 6 across lanes), then add the tail and normalise
+  float r[2], w[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float x = 0.f, y = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x += red[k][2 * lane + c];
+      y += red[k][kCh + 2 * lane + c];
+    }
+    r[c] = x;
+    w[c] = y;
+  }
+  float Lt = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) Lt += lsum[k];
+  {
+    const float a0 = r[0] + r[1], a1 = r[0] - r[1];
+    r[0] = a0;
+    r[1] = a1;
+  }
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const bool upper = (lane >> b) & 1;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float o = __shfl_xor(r[c], 1 << b);
+      r[c] = upper ? o - r[c] : r[c] + o;
+    }
+  }
+  const float inv_l = Lt > 0.f ? 1.0f / Lt : 0.f;
+  constexpr float kInvSqrt128 = 0.08838834764831845f;
+  _Float16* o = out + static_cast<int64_t>(sq) * kCh + 2 * lane;
+  o[0] = static_cast<_Float16>((r[0] * kInvSqrt128 + w[0]) * inv_l);
+  o[1] = static_cast<_Float16>((r[1] * kInvSqrt128 + w[1]) * inv_l);
 }
 
 DecodePlan plan_decode(int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq) {
@@ -602,8 +634,8 @@ static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64
                      plan.n_splits, plan.groups_per_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_kernel<G>), dim3(num_seqs * num_kv_heads), dim3(256), 0, stream, q, workspace,
-                     plan.n_splits, seq_lens, tail_k, tail_v, num_q_heads, num_kv_heads, sm_scale * kLog2e, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(num_seqs * num_q_heads), dim3(256), 0, stream, q, workspace, plan.n_splits,
+                     seq_lens, tail_k, tail_v, num_q_heads, G, sm_scale * kLog2e, out);
   return hipGetLastError();
 }
 

@@ -24,8 +24,9 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq);
 
-// Workspace floats per (sequence, query head, split): running max, running sum, 128 accumulators.
-constexpr int kPartialFloats = 130;
+// Workspace floats per (sequence, query head, split): running max, running sum, two pad floats
+// (16-byte alignment of what follows), 128 accumulators.
+constexpr int kPartialFloats = 132;
 
 bool decode_supported(int kb, int vb, int group_size);
 

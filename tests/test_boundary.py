@@ -56,7 +56,7 @@ def test_record_and_workspace_sizes():
     assert kv.record_bytes(f) == 15360
     assert kv.record_bytes(kv.format_parse("kvarn_k8v8_g128")) == 35840
     ws = kv.decode_workspace_bytes(f, 32, 32, 4, 128)
-    assert ws > 0 and ws % (130 * 4) == 0
+    assert ws > 0 and ws % (132 * 4) == 0   # 132 floats per (seq, q head, split)
     assert kv.decode_workspace_bytes(f, 32, 24, 4, 128) == 0   # G = 6 unsupported
     assert kv.decode_workspace_bytes(f, 32, 30, 4, 128) == 0   # Hq % Hkv != 0
     bad = kv.Format(4, 2, 128, 64, 128, 8)

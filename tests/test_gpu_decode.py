@@ -129,12 +129,16 @@ def test_decode_page_permutation_and_split_invariance():
     pt2 = perm[st.pt].astype(np.int32)
     out2 = st.run_gpu(pt=pt2, cache=torch.from_numpy(moved.reshape(-1)).to(DEV))
     assert np.array_equal(out2, base)
-    # a wider page table changes the split-K grid: results agree to fp16 rounding
+    # a wider page table changes the split-K grid, hence the running maxima at which the fp16
+    # PV weights are rounded.  That rounding gives each layout a relative output error of order
+    # 2^-12 whatever the context length (signal and error average down alike), so two layouts
+    # agree to within the fp16 unit roundoff 2^-11, a quarter of the decode tolerance
     wide = np.concatenate([st.pt, np.repeat(st.pt[:, -1:], 300, axis=1)], axis=1)
     out3 = st.run_gpu(pt=wide)
-    d = np.abs(out3.astype(np.float64) - base.astype(np.float64))
-    tol = 2.0 ** -10 * np.maximum(np.abs(base.astype(np.float64)), 2.0 ** -14)
-    assert np.all(d <= tol)
+    b64, o64 = base.astype(np.float64), out3.astype(np.float64)
+    rel = np.linalg.norm(o64 - b64, axis=-1) / np.maximum(np.linalg.norm(b64, axis=-1), 1e-30)
+    print(f"split change: max row rel L2 {rel.max():.3g}")
+    assert rel.max() <= 2.0 ** -11
     _compare(base, st.run_oracle(), st.lens)
 
 
