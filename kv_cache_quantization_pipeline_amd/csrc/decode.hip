@@ -53,6 +53,10 @@ __device__ __forceinline__ f16x8 cat4(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
 template <int KB>
 struct KRegs;
 template <>
+struct KRegs<2> {
+  u32x2 w;
+};
+template <>
 struct KRegs<4> {
   u32x4 w;
 };
@@ -63,7 +67,9 @@ struct KRegs<8> {
 
 template <int KB>
 __device__ __forceinline__ void load_k(KRegs<KB>& r, const uint8_t* p) {
-  if constexpr (KB == 4) {
+  if constexpr (KB == 2) {
+    r.w = *reinterpret_cast<const u32x2*>(p);
+  } else if constexpr (KB == 4) {
     r.w = *reinterpret_cast<const u32x4*>(p);
   } else {
     r.w[0] = *reinterpret_cast<const u32x4*>(p);
@@ -75,13 +81,23 @@ __device__ __forceinline__ void load_k(KRegs<KB>& r, const uint8_t* p) {
 // i.e. channel 4*gr + kb + 16*keperm(s).
 template <int KB>
 __host__ __device__ constexpr int keperm(int s) {
-  return KB == 4 ? (s < 4 ? 2 * s : 2 * (s - 4) + 1)  // 0 2 4 6 1 3 5 7
-                 : ((s & 4) | ((s & 1) << 1) | ((s >> 1) & 1));  // 0 2 1 3 4 6 5 7
+  return KB == 2   ? ((s >> 1) | ((s & 1) << 2))                    // 0 4 1 5 2 6 3 7
+         : KB == 4 ? (s < 4 ? 2 * s : 2 * (s - 4) + 1)              // 0 2 4 6 1 3 5 7
+                   : ((s & 4) | ((s & 1) << 1) | ((s >> 1) & 1));   // 0 2 1 3 4 6 5 7
 }
 
 template <int KB>
 __device__ __forceinline__ f16x8 dequant_k(const KRegs<KB>& r, int kb) {
-  if constexpr (KB == 4) {
+  if constexpr (KB == 2) {
+    // units 2j and 2j+1 share a dword; (w >> 2i) & 0x03030303 holds codes e = i and i + 4 of
+    // both, one per byte; the conversion's byte pair picks the unit
+    const uint32_t w = r.w[kb >> 1];
+    const uint32_t m0 = w & 0x03030303u, m1 = (w >> 2) & 0x03030303u, m2 = (w >> 4) & 0x03030303u,
+                   m3 = (w >> 6) & 0x03030303u;
+    if (kb & 1)
+      return cat4(fp8b_to_f16<true>(m0), fp8b_to_f16<true>(m1), fp8b_to_f16<true>(m2), fp8b_to_f16<true>(m3));
+    return cat4(fp8b_to_f16<false>(m0), fp8b_to_f16<false>(m1), fp8b_to_f16<false>(m2), fp8b_to_f16<false>(m3));
+  } else if constexpr (KB == 4) {
     const uint32_t w = r.w[kb];
     const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
     return cat4(fp8b_to_f16<false>(lo), fp8b_to_f16<true>(lo), fp8b_to_f16<false>(hi), fp8b_to_f16<true>(hi));
@@ -99,6 +115,10 @@ struct VRegs<2> {
   u32x2 w;  // half 0, half 1
 };
 template <>
+struct VRegs<4> {
+  u32x4 w;  // half 0: w[0], w[1]; half 1: w[2], w[3]
+};
+template <>
 struct VRegs<8> {
   u32x4 w[2];
 };
@@ -107,19 +127,32 @@ template <int VB>
 __device__ __forceinline__ void load_v(VRegs<VB>& r, const uint8_t* p) {
   if constexpr (VB == 2) {
     r.w = *reinterpret_cast<const u32x2*>(p);
+  } else if constexpr (VB == 4) {
+    r.w = *reinterpret_cast<const u32x4*>(p);
   } else {
     r.w[0] = *reinterpret_cast<const u32x4*>(p);
     r.w[1] = *reinterpret_cast<const u32x4*>(p + 16);
   }
 }
 
-// k-step kb covers tokens 32*kb + 16*h + 4*gr + i; register r holds slots
-// (2r, 2r+1) = tokens (h = 0, i = r), (h = 1, i = r).
+// k-step kb covers tokens 32*kb + 16*h + 4*gr + i (h, i < 2, 4); slot vslot<VB>(h, i) of the
+// MFMA operand holds token (h, i): (2i + h) for 2 and 8 bits; for 4 bits the order the byte masks
+// produce, slots (0 1 2 3 4 5 6 7) = (h,i) (0,0) (0,2) (1,0) (1,2) (0,1) (0,3) (1,1) (1,3).
+template <int VB>
+__host__ __device__ constexpr int vslot(int h, int i) {
+  return VB == 4 ? (((i & 1) << 2) | (h << 1) | (i >> 1)) : (2 * i + h);
+}
+
 template <int VB, int WS>
 __device__ __forceinline__ f16x8 dequant_v_ws(const VRegs<VB>& r, int half) {
   constexpr int ws = WS;
   const int kb = 2 * half + WS;
-  if constexpr (VB == 2) {
+  if constexpr (VB == 4) {
+    // dword 2 half + WS holds token (h, i) at bit 16 h + 4 i
+    const uint32_t d = r.w[2 * half + WS];
+    const uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu;
+    return cat4(fp8b_to_f16<false>(lo), fp8b_to_f16<true>(lo), fp8b_to_f16<false>(hi), fp8b_to_f16<true>(hi));
+  } else if constexpr (VB == 2) {
     const uint32_t d = r.w[half];
     return cat4(fp8b_to_f16<WS>(d & 0x03030303u), fp8b_to_f16<WS>((d >> 2) & 0x03030303u),
                 fp8b_to_f16<WS>((d >> 4) & 0x03030303u), fp8b_to_f16<WS>((d >> 6) & 0x03030303u));
@@ -178,13 +211,21 @@ __device__ __forceinline__ f16x8 zero8() {
 
 }  // namespace
 
+// Pages per wave step: 16/G fills the 16 MFMA columns (page, head); where the codes of 16/G pages
+// would not fit in the registers of two waves per SIMD (8-bit K or V codes with G = 8), one page
+// per step and the columns of the missing page masked.
+template <int KB, int VB, int G>
+__host__ __device__ constexpr int decode_pages_per_step() {
+  return (G == 8 && (KB == 8 || VB == 8)) ? 1 : 16 / G;
+}
+
 template <int KB, int VB, int G>
 __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ cache,
                                                         int64_t page_stride, const int32_t* __restrict__ page_table,
                                                         int max_pages, const int32_t* __restrict__ seq_lens,
                                                         int num_q_heads, int num_kv_heads, float qscale,
                                                         float* __restrict__ ws, int n_splits, int groups_per_split) {
-  constexpr int P = 16 / G;
+  constexpr int P = decode_pages_per_step<KB, VB, G>();
   constexpr int R = record_bytes(KB, VB);
   constexpr int SC = 6 * kCh;   // floats of scales per page
   constexpr int MRG = 130;      // floats per merged row
@@ -231,10 +272,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   }
   __syncthreads();
 
-  // this lane's QK column / PV row n = nl: page e_own of the group, head g_own
+  // this lane's QK column / PV row n = nl: page e_own of the group, head g_own.  With P*G < 16
+  // the columns of pages e_own >= P are unused: zero B operand, masked logits, zero weights.
   const int e_own = nl / G;
   const int g_own = nl - e_own * G;
+  const bool col_ok = e_own < P;
+  const int e_oc = col_ok ? e_own : 0;
   const int e_row = (4 * gr) / G;  // page of the PV result rows 4*gr .. 4*gr+3 held by this lane
+  const int e_rc = e_row < P ? e_row : 0;
 
   f16x8 ONES;
 #pragma unroll
@@ -285,8 +330,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
     for (int k = 0; k < 3 * P; ++k) reinterpret_cast<float4*>(sb)[lane + 64 * k] = cur.sc[k];
     __builtin_amdgcn_wave_barrier();
 
-    const bool valid_own = gi * P + e_own < n_pages;
-    const float* sown = sb + e_own * SC;
+    const bool valid_own = col_ok && gi * P + e_own < n_pages;
+    const float* sown = sb + e_oc * SC;
 
     // q'' = c_K ⊙ q' for this lane's page, as the QK B operand, split into fp16 hi + lo parts
     // (q'' = hi + lo to ~22 bits) so that rounding q'' does not perturb the logits
@@ -295,7 +340,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
     for (int e8 = 0; e8 < 8; ++e8) {
       const float4 c4 = *reinterpret_cast<const float4*>(sown + 4 * gr + 16 * e8);
       const float4 q4 = *reinterpret_cast<const float4*>(&qrot[g_own][4 * gr + 16 * e8]);
-      const float x[4] = {c4.x * q4.x, c4.y * q4.y, c4.z * q4.z, c4.w * q4.w};
+      const float x[4] = {col_ok ? c4.x * q4.x : 0.f, col_ok ? c4.y * q4.y : 0.f, col_ok ? c4.z * q4.z : 0.f,
+                          col_ok ? c4.w * q4.w : 0.f};
 #pragma unroll
       for (int sl = 0; sl < 8; ++sl)
         if (keperm<KB>(sl) == e8) {
@@ -391,8 +437,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
       for (int r = 0; r < 4; ++r) {
         const _Float16 w0 = static_cast<_Float16>(wv[0][r]);
         const _Float16 w1 = static_cast<_Float16>(wv[1][r]);
-        aw[kb][2 * r] = w0;
-        aw[kb][2 * r + 1] = w1;
+        aw[kb][vslot<VB>(0, r)] = w0;
+        aw[kb][vslot<VB>(1, r)] = w1;
         wexact += wv[0][r] + wv[1][r];
         wround += static_cast<float>(w0) + static_cast<float>(w1);
       }
@@ -412,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
     float arow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * gr + i);
-    const float* srow = sb + e_row * SC;
+    const float* srow = sb + e_rc * SC;
 
     // PV: one accumulator per page; the lane keeps its rows' page
 #pragma unroll
@@ -602,9 +648,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
   o[1] = static_cast<_Float16>((r[1] * kInvSqrt128 + w[1]) * inv_l);
 }
 
-DecodePlan plan_decode(int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq) {
+int decode_pages_per_step(int kb, int vb, int group_size) {
+  if (group_size == 8) return (kb == 8 || vb == 8) ? 1 : 2;
+  return 1;
+}
+
+DecodePlan plan_decode(int kb, int vb, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq) {
   DecodePlan p;
-  p.pages_per_group = 16 / group_size;
+  p.pages_per_group = decode_pages_per_step(kb, vb, group_size);
   const int groups_max = (max_pages_per_seq + p.pages_per_group - 1) / p.pages_per_group;
   const int units = num_seqs * num_kv_heads;
   const int target_wgs = 512;  // 2 per CU on 256 CUs
@@ -619,7 +670,7 @@ DecodePlan plan_decode(int num_seqs, int num_kv_heads, int group_size, int max_p
 }
 
 bool decode_supported(int kb, int vb, int group_size) {
-  return (kb == 4 || kb == 8) && (vb == 2 || vb == 8) && (group_size == 8 || group_size == 16);
+  return (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8) && (group_size == 8 || group_size == 16);
 }
 
 template <int KB, int VB, int G>
@@ -648,14 +699,24 @@ hipError_t launch_decode(int kb, int vb, int group_size, const _Float16* q, cons
   if (kb == KB_ && vb == VB_ && group_size == G_)                                                                \
     return launch_decode_t<KB_, VB_, G_>(q, cache, page_stride, page_table, max_pages, seq_lens, tail_k, tail_v, \
                                          sm_scale, out, workspace, num_seqs, num_q_heads, num_kv_heads, plan, stream);
+  KVARN_DECODE_CASE(2, 2, 8)
+  KVARN_DECODE_CASE(2, 4, 8)
+  KVARN_DECODE_CASE(2, 8, 8)
   KVARN_DECODE_CASE(4, 2, 8)
-  KVARN_DECODE_CASE(8, 8, 8)
+  KVARN_DECODE_CASE(4, 4, 8)
   KVARN_DECODE_CASE(4, 8, 8)
   KVARN_DECODE_CASE(8, 2, 8)
+  KVARN_DECODE_CASE(8, 4, 8)
+  KVARN_DECODE_CASE(8, 8, 8)
+  KVARN_DECODE_CASE(2, 2, 16)
+  KVARN_DECODE_CASE(2, 4, 16)
+  KVARN_DECODE_CASE(2, 8, 16)
   KVARN_DECODE_CASE(4, 2, 16)
-  KVARN_DECODE_CASE(8, 8, 16)
+  KVARN_DECODE_CASE(4, 4, 16)
   KVARN_DECODE_CASE(4, 8, 16)
   KVARN_DECODE_CASE(8, 2, 16)
+  KVARN_DECODE_CASE(8, 4, 16)
+  KVARN_DECODE_CASE(8, 8, 16)
 #undef KVARN_DECODE_CASE
   return hipErrorInvalidValue;
 }

@@ -16,13 +16,14 @@ hipError_t launch_append(const _Float16* k_new, const _Float16* v_new, int32_t* 
                          hipStream_t stream);
 
 // Split-K decode plan: the grid is (num_seqs*num_kv_heads, n_splits) workgroups of 4 waves;
-// a split covers groups_per_split groups of P = 16/G pages, groups_per_split / 4 per wave.
+// a split covers groups_per_split groups of pages_per_group pages, groups_per_split / 4 per wave.
 struct DecodePlan {
   int pages_per_group;
   int groups_per_split;
   int n_splits;
 };
-DecodePlan plan_decode(int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq);
+int decode_pages_per_step(int kb, int vb, int group_size);
+DecodePlan plan_decode(int kb, int vb, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq);
 
 // Workspace floats per (sequence, query head, split): running max, running sum, two pad floats
 // (16-byte alignment of what follows), 128 accumulators.

@@ -73,7 +73,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int
     return 0;
   const int G = num_q_heads / num_kv_heads;
   if (G != 8 && G != 16) return 0;
-  const kvarn::DecodePlan plan = kvarn::plan_decode(num_seqs, num_kv_heads, G, max_pages_per_seq);
+  const kvarn::DecodePlan plan = kvarn::plan_decode(f->k_bits, f->v_bits, num_seqs, num_kv_heads, G, max_pages_per_seq);
   return static_cast<size_t>(num_seqs) * num_q_heads * plan.n_splits * kvarn::kPartialFloats * sizeof(float);
 }
 
@@ -135,7 +135,7 @@ kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int
   if (workspace_bytes < kvarn_decode_workspace_bytes(f, num_seqs, num_q_heads, num_kv_heads, max_pages_per_seq))
     return KVARN_E_INVALID_ARG;
   if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
-  const kvarn::DecodePlan plan = kvarn::plan_decode(num_seqs, num_kv_heads, G, max_pages_per_seq);
+  const kvarn::DecodePlan plan = kvarn::plan_decode(f->k_bits, f->v_bits, num_seqs, num_kv_heads, G, max_pages_per_seq);
   if (plan.n_splits > 65535) return KVARN_E_UNSUPPORTED;
   return hip_status(kvarn::launch_decode(f->k_bits, f->v_bits, G, static_cast<const _Float16*>(q),
                                          static_cast<const uint8_t*>(cache), page_stride_bytes, page_table,

@@ -104,7 +104,10 @@ def test_calls_reject_bad_arguments_before_launch():
     assert dec(ws=ctypes.c_void_p(0x1004)) == kv.KVARN_E_INVALID_ARG
     assert dec(q=None) == kv.KVARN_E_INVALID_ARG
     assert dec(stride=R) == kv.KVARN_E_INVALID_ARG
-    assert dec(fmt=ctypes.byref(kv.format_parse("kvarn_k2v4_g128"))) == kv.KVARN_E_UNSUPPORTED
+    # every bit-width pair of the dtype family decodes
+    for kb in (2, 4, 8):
+        for vb in (2, 4, 8):
+            assert kv.decode_workspace_bytes(kv.format_parse(f"kvarn_k{kb}v{vb}_g128"), 2, 16, 2, 4) > 0
     assert dec(nseq=0) == kv.KVARN_OK
     del args
 

@@ -93,7 +93,7 @@ def _compare(gpu, ref, lens):
     return worst
 
 
-@pytest.mark.parametrize("name", ["kvarn_k4v2_g128", "kvarn_k8v8_g128", "kvarn_k4v8_g128", "kvarn_k8v2_g128"])
+@pytest.mark.parametrize("name", [f"kvarn_k{kb}v{vb}_g128" for kb in (2, 4, 8) for vb in (2, 4, 8)])
 @pytest.mark.parametrize("G", [8, 16])
 def test_decode_ragged_small(name, G):
     lens = [326, 128, 5, 0, 1, 1029, 640, 127]
