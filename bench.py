@@ -43,6 +43,10 @@ def parse():
                     help="wall seconds per oracle leg (quantise, decode) of the CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for scaling PMC byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no benchmark: turn the counter_collection.csv files of two rocprofv3 --pmc runs of "
+                         "this script (FETCH_SIZE, then WRITE_SIZE; both with --copy-calibration-mib N) into "
+                         "profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -65,6 +69,53 @@ def load_traffic(src_hash):
     if t.get("source_hash") != src_hash:
         return {}
     return t.get("kernels", {})
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib):
+    """HBM bytes per launch of the two timed kernels from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+    (KiB per dispatch), each scaled by the factor that maps the same counter of a plain copy of
+    copy_mib MiB onto the bytes that copy moves."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = r["Dispatch_Id"]
+                rows.setdefault(key, [r["Kernel_Name"], int(r["Grid_Size"]), 0.0])[2] += float(r["Counter_Value"])
+        return list(rows.values())
+
+    if copy_mib <= 0:
+        raise SystemExit("--traffic-from needs --copy-calibration-mib N (the copy size of the profiled runs)")
+    copy_bytes = copy_mib * (1 << 20)
+    out = {"source_hash": source_hash(), "unit": "bytes per launch", "copy_calibration_bytes": copy_bytes,
+           "kernels": {}, "factors": {}}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = per_dispatch(path, counter)
+        copies = [v for name, grid, v in rows if "copyBuffer" in name]
+        if not copies:
+            raise SystemExit(f"{path}: no copy kernel dispatch to calibrate against")
+        factor = copy_bytes / (max(copies) * 1024.0)
+        out["factors"][counter] = factor
+        q_grid = Q_TILES * Q_HKV * 256
+        quant = [v for name, grid, v in rows if "quantize_tiles_kernel" in name and grid == q_grid]
+        dec = [v for name, grid, v in rows if "decode_kernel" in name]
+        comb = [v for name, grid, v in rows if "combine_kernel" in name]
+        if not quant or not dec or not comb:
+            raise SystemExit(f"{path}: missing quantize/decode/combine dispatches")
+        per.setdefault("quantize_tiles", 0.0)
+        per["quantize_tiles"] += sum(quant) / len(quant) * 1024.0 * factor
+        per.setdefault("decode_attention", 0.0)
+        per["decode_attention"] += (sum(dec) / len(dec) + sum(comb) / len(comb)) * 1024.0 * factor
+    out["kernels"] = {k: int(round(v)) for k, v in per.items()}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(k1, v1, seconds):
@@ -114,6 +165,9 @@ def cpu_baseline(k1, v1, seconds):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args.traffic_from[0], args.traffic_from[1], args.copy_calibration_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU; the method needs no cross-GPU exchange "
