@@ -173,36 +173,90 @@ __device__ __forceinline__ f16x8 dequant_v(const VRegs<VB>& r, int kb) {
   return (kb & 1) ? dequant_v_ws<VB, 1>(r, kb >> 1) : dequant_v_ws<VB, 0>(r, kb >> 1);
 }
 
-template <int KB, int VB, int P>
-struct Pair {
-  KRegs<KB> kq[P][8];
-  VRegs<VB> vq[P][8];
-  float4 sc[3 * P];  // the P pages' six scale arrays, 16 bytes per chunk
+// K codes of token blocks mb = 4 h .. 4 h + 3 (h = 0, 1) of the P pages of a group
+template <int KB, int P>
+struct KHalf {
+  KRegs<KB> k[P][4];
+};
+template <int VB, int P>
+struct VAll {
+  VRegs<VB> v[P][8];
 };
 
-template <int KB, int VB, int P>
-__device__ __forceinline__ void load_pair(Pair<KB, VB, P>& d, const uint8_t* const (&rec)[P], int lane) {
-  constexpr int SOFF = scale_offset(KB, VB);
-  const int nl = lane & 15, gr = lane >> 4;
-#pragma unroll
-  for (int k = 0; k < 3 * P; ++k) {
-    const int c = lane + 64 * k;
-    d.sc[k] = *reinterpret_cast<const float4*>(rec[c / 192] + SOFF + (c % 192) * 16);
-  }
-#pragma unroll
-  for (int e = 0; e < P; ++e)
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) load_k<KB>(d.kq[e][mb], rec[e] + (16 * mb + nl) * 16 * KB + 4 * gr * KB);
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited for), gfx9 encoding: vmcnt bits 3:0 and 15:14.
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int KB, int VB, int P>
-__device__ __forceinline__ void load_pair_v(Pair<KB, VB, P>& d, const uint8_t* const (&rec)[P], int lane) {
-  const int nl = lane & 15, gr = lane >> 4;
+// Loads of one group go through buffer descriptors (one per page, base = the record): the lane's
+// offset is one VGPR per operand kind and the block offset an SGPR, so no per-lane 64-bit address
+// is computed or kept live across the group loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// K codes of token blocks 4h .. 4h+3: token 16 mb + nl, units 4 gr .. 4 gr + 3
+template <int KB, int P>
+__device__ __forceinline__ void load_k_half(KHalf<KB, P>& d, const __amdgpu_buffer_rsrc_t (&rs)[P], int h, int lane) {
+  const uint32_t lo = static_cast<uint32_t>((lane & 15) * 16 * KB + 4 * (lane >> 4) * KB);
 #pragma unroll
   for (int e = 0; e < P; ++e)
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      load_v<VB>(d.vq[e][nb], rec[e] + k_code_bytes(KB) + ((nb * 4 + gr) * 16 + nl) * 4 * VB);
+    for (int m = 0; m < 4; ++m) {
+      const int off = 16 * (4 * h + m) * 16 * KB;
+      if constexpr (KB == 2) {
+        d.k[e][m].w = bload64(rs[e], lo, off);
+      } else if constexpr (KB == 4) {
+        d.k[e][m].w = bload128(rs[e], lo, off);
+      } else {
+        d.k[e][m].w[0] = bload128(rs[e], lo, off);
+        d.k[e][m].w[1] = bload128(rs[e], lo, off + 16);
+      }
+    }
+}
+
+// V codes: unit (nb, gr, nl) of 4 VB bytes at k_code_bytes + (64 nb + lane) 4 VB
+template <int KB, int VB, int P>
+__device__ __forceinline__ void load_v_all(VAll<VB, P>& d, const __amdgpu_buffer_rsrc_t (&rs)[P], int lane) {
+  const uint32_t lo = static_cast<uint32_t>(lane * 4 * VB);
+#pragma unroll
+  for (int e = 0; e < P; ++e)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const int off = k_code_bytes(KB) + nb * 64 * 4 * VB;
+      if constexpr (VB == 2) {
+        d.v[e][nb].w = bload64(rs[e], lo, off);
+      } else if constexpr (VB == 4) {
+        d.v[e][nb].w = bload128(rs[e], lo, off);
+      } else {
+        d.v[e][nb].w[0] = bload128(rs[e], lo, off);
+        d.v[e][nb].w[1] = bload128(rs[e], lo, off + 16);
+      }
+    }
+}
+
+// The P pages' six scale arrays (3 KB each, verbatim) into this wave's LDS stage, 1 KB per
+// global_load_lds_dwordx4 (asynchronous, no registers; the compiler waits for it before the first
+// read of that stage).
+template <int KB, int VB, int P>
+__device__ __forceinline__ void copy_scales(float* stage, const uint8_t* const (&rec)[P], int lane) {
+  const uint32_t lo = static_cast<uint32_t>(lane * 16);
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    const uint8_t* sbase = rec[e] + scale_offset(KB, VB);
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      __builtin_amdgcn_global_load_lds(sbase + (lo + static_cast<uint32_t>(c * 1024)), stage + e * 6 * kCh + c * 256, 16,
+                                       0, 0);
+  }
 }
 
 __device__ __forceinline__ f16x8 zero8() {
@@ -231,10 +285,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   constexpr int MRG = 130;      // floats per merged row
 
   __shared__ float qrot[G][kCh];
-  // per wave: staged scales of the current group (P pages); reused for the merge
+  // Per wave, the scales of the current group and of the next one (P pages each): two stages, so
+  // that the next group's scales are copied in while this group is computed.  They are separate
+  // arrays, so that the compiler tells the copy into one from the reads of the other.  The final
+  // merge reuses them (waves 0-1 in the first, 2-3 in the second).
   constexpr int STAGE_FLOATS = 4 * P * SC;
-  constexpr int MERGE_FLOATS = 4 * 16 * MRG;
-  __shared__ float lds[STAGE_FLOATS > MERGE_FLOATS ? STAGE_FLOATS : MERGE_FLOATS];
+  constexpr int MERGE_HALF = 2 * 16 * MRG;
+  constexpr int BUF = STAGE_FLOATS > MERGE_HALF ? STAGE_FLOATS : MERGE_HALF;
+  __shared__ __attribute__((aligned(16))) float stage0[BUF];
+  __shared__ __attribute__((aligned(16))) float stage1[BUF];
 
   const int sh = blockIdx.x;
   const int s = sh / num_kv_heads;
@@ -298,37 +357,43 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   const int gpw = groups_per_split / 4;
   const int g_begin = sp * groups_per_split + wave * gpw;
   const int g_end = min(g_begin + gpw, n_groups);
-  float* const sb = lds + wave * (P * SC);
   const int64_t pt_row = static_cast<int64_t>(s) * max_pages;
   const int64_t head_off = static_cast<int64_t>(h) * R;
 
-  // Physical page ids of a group: a vector load (lane e < P holds page e of the group), issued one
-  // group ahead so that its latency hides behind the current group; read out with readlane.
-  auto page_ids = [&](int gi) -> int {
-    const int pg = gi * P + (lane & (P - 1));
-    return page_table[pt_row + (pg < n_pages ? pg : gi * P)];
+  // Physical page ids of this wave's groups: one vector load for 64 pages at a time (lane l holds
+  // page base * P + l, clamped to the last page: a missing second page of a group is masked),
+  // read out with readlane.
+  int ids_base = g_begin, ids = 0;
+  auto load_ids = [&](int g0) {
+    ids_base = g0;
+    const int pg = min(g0 * P + lane, n_pages - 1);
+    ids = page_table[pt_row + pg];
   };
-  auto recs = [&](int ids, const uint8_t* (&rec)[P]) {
+  auto recs = [&](int gi, const uint8_t* (&rec)[P]) {
+    if ((gi - ids_base) * P + P > 64) load_ids(gi);
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      const int phys = __builtin_amdgcn_readlane(ids, e);
+      const int phys = __builtin_amdgcn_readlane(ids, (gi - ids_base) * P + e);
       rec[e] = cache + static_cast<int64_t>(phys) * page_stride + head_off;
     }
   };
 
-  // One group: load its K codes and scales, stage the scales in LDS, compute; the V codes are
-  // loaded once QK is done, into the registers of the consumed K codes (register budget of two
-  // waves per SIMD).  Two waves share each SIMD, so one wave's loads overlap the other's
-  // arithmetic.
-  auto step = [&](int gi, int ids, int& ids_next) {
-    Pair<KB, VB, P> cur;
-    const uint8_t* rec[P];
-    recs(ids, rec);
-    load_pair<KB, VB, P>(cur, rec, lane);
-    if (gi + 1 < g_end) ids_next = page_ids(gi + 1);
+  // One group, software-pipelined over the groups of the wave.  On entry the K codes of token
+  // blocks 0-3 (kpre) and the scales (LDS stage sb) are in flight or arrived, issued at the end of
+  // the previous group.  The wave issues blocks 4-7, builds the B operand, computes QK, loads the
+  // V codes into the registers of the consumed K codes, computes softmax and PV, then issues the
+  // next group's blocks 0-3 and copies its scales into the other stage (sb_next).
+  auto step = [&](int gi, const KHalf<KB, P>& kpre, KHalf<KB, P>& kpre_next, const float* sb, float* sb_next,
+                  const uint8_t* const (&rec)[P], const uint8_t* (&rec_next)[P]) {
+    __amdgpu_buffer_rsrc_t rs[P];
 #pragma unroll
-    for (int k = 0; k < 3 * P; ++k) reinterpret_cast<float4*>(sb)[lane + 64 * k] = cur.sc[k];
-    __builtin_amdgcn_wave_barrier();
+    for (int e = 0; e < P; ++e) rs[e] = record_rsrc(rec[e], R);
+    KHalf<KB, P> khi;
+    load_k_half<KB, P>(khi, rs, 1, lane);
+    // Vector memory operations complete in order: waiting until only the loads just issued are
+    // outstanding means the scale copy into sb (and kpre) issued at the end of the previous group
+    // has landed.  The compiler's own tracking of LDS copies does not see it through this loop.
+    vmcnt_wait<P * 4 * (KB == 8 ? 2 : 1)>();
 
     const bool valid_own = col_ok && gi * P + e_own < n_pages;
     const float* sown = sb + e_oc * SC;
@@ -376,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
         d[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const f16x8 a = dequant_k<KB>(cur.kq[e][mb], kb);
+          const f16x8 a = dequant_k<KB>(mb < 4 ? kpre.k[e][mb] : khi.k[e][mb - 4], kb);
           d[e] = mfma16(a, bqh[kb], d[e]);
           d[e] = mfma16(a, bql[kb], d[e]);
         }
@@ -393,7 +458,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
     }
 
     __builtin_amdgcn_sched_barrier(0);
-    load_pair_v<KB, VB, P>(cur, rec, lane);
+    VAll<VB, P> vc;
+    load_v_all<KB, VB, P>(vc, rs, lane);
 
     // online softmax for column nl
     float mloc = -INFINITY;
@@ -468,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
       for (int e = 0; e < P; ++e) {
         d[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) d[e] = mfma16(aw[kb], dequant_v<VB>(cur.vq[e][nb], kb), d[e]);
+        for (int kb = 0; kb < 4; ++kb) d[e] = mfma16(aw[kb], dequant_v<VB>(vc.v[e][nb], kb), d[e]);
       }
       f32x4 dd = d[0];
 #pragma unroll
@@ -478,21 +544,46 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv * dd[i]);
     }
+    // the next group's K codes of blocks 0-3 and its scales, in flight while the next step starts
+    __builtin_amdgcn_sched_barrier(0);
+    if (gi + 1 < g_end) {
+      recs(gi + 1, rec_next);
+      __amdgpu_buffer_rsrc_t rs_n[P];
+#pragma unroll
+      for (int e = 0; e < P; ++e) rs_n[e] = record_rsrc(rec_next[e], R);
+      load_k_half<KB, P>(kpre_next, rs_n, 0, lane);
+      copy_scales<KB, VB, P>(sb_next, rec_next, lane);
+    }
     __builtin_amdgcn_wave_barrier();
   };
 
   if (g_begin < g_end) {
-    int ids = page_ids(g_begin), ids_next = 0;
-    for (int gi = g_begin; gi < g_end; ++gi) {
-      step(gi, ids, ids_next);
-      ids = ids_next;
+    float* const sb0 = stage0 + wave * (P * SC);
+    float* const sb1 = stage1 + wave * (P * SC);
+    KHalf<KB, P> ka, kb2;
+    const uint8_t* ra[P];
+    const uint8_t* rb[P];
+    load_ids(g_begin);
+    recs(g_begin, ra);
+    {
+      __amdgpu_buffer_rsrc_t rs[P];
+#pragma unroll
+      for (int e = 0; e < P; ++e) rs[e] = record_rsrc(ra[e], R);
+      load_k_half<KB, P>(ka, rs, 0, lane);
+      copy_scales<KB, VB, P>(sb0, ra, lane);
+    }
+    for (int gi = g_begin; gi < g_end; gi += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      step(gi, ka, kb2, sb0, sb1, ra, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (gi + 1 < g_end) step(gi + 1, kb2, ka, sb1, sb0, rb, ra);
     }
   }
 
   // ---- merge the 4 waves x P streams of each head, write one partial per head ----------
   const float l_col = rows_sum4(l_part);
-  __syncthreads();  // staging buffers are reused below
-  float* mrg = lds + wave * 16 * MRG;
+  __syncthreads();  // the stages are reused below
+  float* mrg = (wave < 2 ? stage0 : stage1) + (wave & 1) * 16 * MRG;
   if (gr == 0) {
     mrg[nl * MRG + 0] = m_run;
     mrg[nl * MRG + 1] = l_col;
@@ -509,14 +600,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int e = 0; e < P; ++e) M = fmaxf(M, lds[(w * 16 + e * G + g) * MRG]);
+      for (int e = 0; e < P; ++e) M = fmaxf(M, (w < 2 ? stage0 : stage1)[((w & 1) * 16 + e * G + g) * MRG]);
     float L = 0.f, A = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < 4; ++w)
 #pragma unroll
         for (int e = 0; e < P; ++e) {
-          const float* row = lds + (w * 16 + e * G + g) * MRG;
+          const float* row = (w < 2 ? stage0 : stage1) + ((w & 1) * 16 + e * G + g) * MRG;
           const float f = __builtin_amdgcn_exp2f(row[0] - M);
           L = fmaf(row[1], f, L);
           A = fmaf(row[2 + j], f, A);
