@@ -57,15 +57,35 @@ __device__ __forceinline__ void rows_allgather4(float s, float (&v)[4]) {
   v[3] = g;
 }
 
+// Pack codes c = 0 .. N-1 (unrounded value f(c)) at bit BITS*c of the words w: code c goes to byte
+// (BITS*c % 32) / 8 of sub-word (BITS*c % 8) / BITS through v_cvt_pk_u8_f32 (round to nearest,
+// ties to even, clamp to [0, 255], insert as one byte), and the 8/BITS sub-words of a word are
+// merged with shifts by BITS.
+template <int BITS, int N, class F, int NW>
+__device__ __forceinline__ void pack_codes(F f, uint32_t (&w)[NW]) {
+  constexpr int NS = 8 / BITS;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    uint32_t d[NS];
+#pragma unroll
+    for (int sw = 0; sw < NS; ++sw) d[sw] = 0;
+#pragma unroll
+    for (int c = 0; c < N; ++c)
+      if ((BITS * c) / 32 == k)
+        d[(BITS * c % 8) / BITS] = __builtin_amdgcn_cvt_pk_u8_f32(f(c), (BITS * c % 32) / 8, d[(BITS * c % 8) / BITS]);
+    uint32_t u = d[0];
+#pragma unroll
+    for (int sw = 1; sw < NS; ++sw) u |= d[sw] << (BITS * sw);
+    w[k] = u;
+  }
+}
+
 // Codes and stores for one tile half once the channel sums S~_j are known.  R holds Ytilde on
 // entry and W = Ytilde exp(-v~) (= Y exp(-v)) afterwards.
 template <int BITS>
 __device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[8], uint8_t* rec, int code_off,
                                                int scale_off, bool is_v, int half, int gr, int nl, WaveLds& L) {
   constexpr int qmax = (1 << BITS) - 1;
-  // fma(d, inv, 1.5*2^23) rounds d*inv to the nearest integer (ties to even) in one step and
-  // leaves that integer in the low mantissa bits (d*inv is in [0, qmax]).
-  constexpr float kRound = 12582912.0f;
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
     const float b = __builtin_amdgcn_rsqf(sfin[nb]);  // exp(-v~_j)
@@ -127,10 +147,14 @@ __device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[
     for (int nb = 0; nb < 8; ++nb) sc[16 * nb + nl] = __builtin_sqrtf(sfin[nb] * (1.0f / 128.0f));
   }
 
-  auto code = [&](int mb, int nb, int i) -> uint32_t {
-    const float f = fmaf(R.y[mb][nb][i] - mnv[mb][i], inv[mb][i], kRound);
-    return as_u(f) & static_cast<uint32_t>(qmax);
-  };
+  // (W - mn) * inv as one FMA; v_cvt_pk_u8_f32 rounds it to the nearest integer (ties to even),
+  // clamps to [0, 255] and inserts it as one byte of a word
+  float nmi[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nmi[mb][i] = -mnv[mb][i] * inv[mb][i];
+  auto val = [&](int mb, int nb, int i) -> float { return fmaf(R.y[mb][nb][i], inv[mb][i], nmi[mb][i]); };
 
   if (!is_v) {
     // K unit of token t, lane nl: channels nl + 16e at bit BITS*e
@@ -141,21 +165,19 @@ __device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[
         const int t = 64 * half + 16 * mb + 4 * gr + i;
         uint8_t* p = rec + code_off + t * 16 * BITS + nl * BITS;
         if constexpr (BITS == 8) {
-          uint32_t lo = 0, hi = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lo |= code(mb, e, i) << (8 * e);
-            hi |= code(mb, e + 4, i) << (8 * e);
-          }
-          *reinterpret_cast<u32x2*>(p) = u32x2{lo, hi};
+          uint32_t w[2];
+          pack_codes<BITS, 8>([&](int e) { return val(mb, e, i); }, w);
+          *reinterpret_cast<u32x2*>(p) = u32x2{w[0], w[1]};
         } else {
-          uint32_t u = 0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) u |= code(mb, e, i) << (BITS * e);
-          if constexpr (BITS == 4)
-            *reinterpret_cast<uint32_t*>(p) = u;
-          else
-            *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(u);
+          // 8 codes: 32 bits (4-bit) or the low 16 bits of a word (2-bit)
+          uint32_t w[1];
+          if constexpr (BITS == 4) {
+            pack_codes<BITS, 8>([&](int e) { return val(mb, e, i); }, w);
+            *reinterpret_cast<uint32_t*>(p) = w[0];
+          } else {
+            pack_codes<BITS, 8>([&](int e) { return val(mb, e, i); }, w);
+            *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(w[0]);
+          }
         }
       }
   } else {
@@ -165,15 +187,7 @@ __device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[
       uint8_t* p = rec + code_off + ((nb * 4 + gr) * 16 + nl) * 4 * BITS + half * 2 * BITS;
       constexpr int W = BITS / 2;  // 32-bit words per unit
       uint32_t u[W];
-#pragma unroll
-      for (int k = 0; k < W; ++k) u[k] = 0;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 4 * mb + i;
-          u[(c * BITS) / 32] |= code(mb, nb, i) << ((c * BITS) % 32);
-        }
+      pack_codes<BITS, 16>([&](int c) { return val(c >> 2, nb, c & 3); }, u);
       if constexpr (W == 1)
         *reinterpret_cast<uint32_t*>(p) = u[0];
       else if constexpr (W == 2)
@@ -301,8 +315,7 @@ __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ 
       rows_allgather4(s1 > 0.f ? s1 : 128.0f, v);
 #pragma unroll
       for (int k = 0; k < 4; ++k) sfin[4 + k] = v[k];
-      break;
-    }
+    } else {
     s0 += kEps;
     s1 += kEps;
     float e[8];
@@ -345,6 +358,7 @@ __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ 
       w[mb][1] = v.y;
       w[mb][2] = v.z;
       w[mb][3] = v.w;
+    }
     }
   }
 
