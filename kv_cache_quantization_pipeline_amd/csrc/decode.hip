@@ -17,8 +17,9 @@
 // operand is block-diagonal (lane column n = (page e, head g) holds q''_e,g for
 // page e's k-steps, zero elsewhere); for PV the A operand is the weights
 // (row (e, g), K over (page, token)), the B operand the V codes.  Codes become
-// exact fp16 integers in registers (4-bit / 2-bit: bytes read as fp8 e4m3 and
-// scaled by 2^9; 8-bit: 0x6400 | byte minus 1024).  Each wave keeps one
+// exact fp16 integers in registers (4-bit: bytes read as fp8 e4m3, scaled by 2^9;
+// 2-bit: nibbles read as fp4 e2m1, scaled by 2; 8-bit: 0x6400 | byte minus
+// 1024).  Each wave keeps one
 // running (max, sum, acc) per MFMA row, i.e. per (page parity, head); the
 // workgroup merges its 4 waves x P streams in LDS and writes one split-K
 // partial per query head.
@@ -39,6 +40,12 @@ template <bool HI>
 __device__ __forceinline__ f16x2 fp8b_to_f16(uint32_t w) {
   // bytes (0,1) or (2,3) of w, each a code 0..15, read as OCP e4m3 (value code * 2^-9) times 2^9
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 512.0f, HI);
+}
+template <int SEL>
+__device__ __forceinline__ f16x2 fp4b_to_f16(uint32_t w) {
+  // byte SEL of w read as two OCP fp4 (e2m1) values, low nibble first: nibbles 0..3 are exactly
+  // 0, 0.5, 1, 1.5, so a 2-bit code alone in its nibble converts to code / 2, times 2
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, SEL);
 }
 __device__ __forceinline__ f16x2 u8pair_to_f16(uint32_t w) {
   // (w & 0x00ff00ff) are two bytes in 16-bit lanes: 0x6400 | b is the fp16 value 1024 + b
@@ -81,22 +88,19 @@ __device__ __forceinline__ void load_k(KRegs<KB>& r, const uint8_t* p) {
 // i.e. channel 4*gr + kb + 16*keperm(s).
 template <int KB>
 __host__ __device__ constexpr int keperm(int s) {
-  return KB == 2   ? ((s >> 1) | ((s & 1) << 2))                    // 0 4 1 5 2 6 3 7
-         : KB == 4 ? (s < 4 ? 2 * s : 2 * (s - 4) + 1)              // 0 2 4 6 1 3 5 7
-                   : ((s & 4) | ((s & 1) << 1) | ((s >> 1) & 1));   // 0 2 1 3 4 6 5 7
+  return KB <= 4 ? (s < 4 ? 2 * s : 2 * (s - 4) + 1)              // 0 2 4 6 1 3 5 7
+                 : ((s & 4) | ((s & 1) << 1) | ((s >> 1) & 1));   // 0 2 1 3 4 6 5 7
 }
 
 template <int KB>
 __device__ __forceinline__ f16x8 dequant_k(const KRegs<KB>& r, int kb) {
   if constexpr (KB == 2) {
-    // units 2j and 2j+1 share a dword; (w >> 2i) & 0x03030303 holds codes e = i and i + 4 of
-    // both, one per byte; the conversion's byte pair picks the unit
+    // units 2j and 2j+1 share a dword (bytes 0-1 and 2-3); w & 0x33333333 leaves codes e = 0, 2 |
+    // 4, 6 of each unit alone in the nibbles of its two bytes, (w >> 2) & 0x33333333 codes 1, 3 | 5, 7
     const uint32_t w = r.w[kb >> 1];
-    const uint32_t m0 = w & 0x03030303u, m1 = (w >> 2) & 0x03030303u, m2 = (w >> 4) & 0x03030303u,
-                   m3 = (w >> 6) & 0x03030303u;
-    if (kb & 1)
-      return cat4(fp8b_to_f16<true>(m0), fp8b_to_f16<true>(m1), fp8b_to_f16<true>(m2), fp8b_to_f16<true>(m3));
-    return cat4(fp8b_to_f16<false>(m0), fp8b_to_f16<false>(m1), fp8b_to_f16<false>(m2), fp8b_to_f16<false>(m3));
+    const uint32_t m0 = w & 0x33333333u, m1 = (w >> 2) & 0x33333333u;
+    if (kb & 1) return cat4(fp4b_to_f16<2>(m0), fp4b_to_f16<3>(m0), fp4b_to_f16<2>(m1), fp4b_to_f16<3>(m1));
+    return cat4(fp4b_to_f16<0>(m0), fp4b_to_f16<1>(m0), fp4b_to_f16<0>(m1), fp4b_to_f16<1>(m1));
   } else if constexpr (KB == 4) {
     const uint32_t w = r.w[kb];
     const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
@@ -136,11 +140,11 @@ __device__ __forceinline__ void load_v(VRegs<VB>& r, const uint8_t* p) {
 }
 
 // k-step kb covers tokens 32*kb + 16*h + 4*gr + i (h, i < 2, 4); slot vslot<VB>(h, i) of the
-// MFMA operand holds token (h, i): (2i + h) for 2 and 8 bits; for 4 bits the order the byte masks
-// produce, slots (0 1 2 3 4 5 6 7) = (h,i) (0,0) (0,2) (1,0) (1,2) (0,1) (0,3) (1,1) (1,3).
+// MFMA operand holds token (h, i): for 2 and 4 bits the order the masks produce, slots
+// (0 1 2 3 4 5 6 7) = (h,i) (0,0) (0,2) (1,0) (1,2) (0,1) (0,3) (1,1) (1,3); (2i + h) for 8 bits.
 template <int VB>
 __host__ __device__ constexpr int vslot(int h, int i) {
-  return VB == 4 ? (((i & 1) << 2) | (h << 1) | (i >> 1)) : (2 * i + h);
+  return VB <= 4 ? (((i & 1) << 2) | (h << 1) | (i >> 1)) : (2 * i + h);
 }
 
 template <int VB, int WS>
@@ -153,9 +157,12 @@ __device__ __forceinline__ f16x8 dequant_v_ws(const VRegs<VB>& r, int half) {
     const uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu;
     return cat4(fp8b_to_f16<false>(lo), fp8b_to_f16<true>(lo), fp8b_to_f16<false>(hi), fp8b_to_f16<true>(hi));
   } else if constexpr (VB == 2) {
+    // byte mb of d holds tokens (mb, i = 0..3) at bits 2i: d & 0x33333333 leaves i = 0, 2 alone in
+    // the nibbles, (d >> 2) & 0x33333333 i = 1, 3; bytes 2 WS, 2 WS + 1 are h = 0, 1
     const uint32_t d = r.w[half];
-    return cat4(fp8b_to_f16<WS>(d & 0x03030303u), fp8b_to_f16<WS>((d >> 2) & 0x03030303u),
-                fp8b_to_f16<WS>((d >> 4) & 0x03030303u), fp8b_to_f16<WS>((d >> 6) & 0x03030303u));
+    const uint32_t m0 = d & 0x33333333u, m1 = (d >> 2) & 0x33333333u;
+    return cat4(fp4b_to_f16<2 * WS>(m0), fp4b_to_f16<2 * WS + 1>(m0), fp4b_to_f16<2 * WS>(m1),
+                fp4b_to_f16<2 * WS + 1>(m1));
   } else {
     const uint32_t D0 = r.w[kb >> 1][2 * ws], D1 = r.w[kb >> 1][2 * ws + 1];
     f16x2 o[4];
