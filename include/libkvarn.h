@@ -123,7 +123,7 @@ kvarn_status kvarn_append_token(const kvarn_format* f, int32_t num_seqs, int32_t
  *              with seq_lens[s] < 128*(max_pages_per_seq + 1); max_pages_per_seq sizes the
  *              split-K grid and the workspace
  *   workspace  (device) >= kvarn_decode_workspace_bytes(...) bytes, 16-byte aligned
- * Supported query heads per kv head: 8 and 16. */
+ * Supported query heads per kv head: 1, 2, 4, 8 and 16. */
 kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
                                     int32_t num_kv_heads, const void* q, const void* cache,
                                     int64_t page_stride_bytes, const int32_t* page_table,

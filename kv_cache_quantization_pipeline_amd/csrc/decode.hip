@@ -272,12 +272,12 @@ __device__ __forceinline__ f16x8 zero8() {
 
 }  // namespace
 
-// Pages per wave step: 16/G fills the 16 MFMA columns (page, head); where the codes of 16/G pages
-// would not fit in the registers of two waves per SIMD (8-bit K or V codes with G = 8), one page
-// per step and the columns of the missing page masked.
+// Pages per wave step P: the 16 MFMA columns are (page, head) pairs.  G = 16 fills them with one
+// page; otherwise a step is two pages (the most whose codes fit the registers of two waves per
+// SIMD), or one for 8-bit K or V codes, and the columns beyond P*G are masked.
 template <int KB, int VB, int G>
 __host__ __device__ constexpr int decode_pages_per_step() {
-  return (G == 8 && (KB == 8 || VB == 8)) ? 1 : 16 / G;
+  return G >= 16 ? 1 : ((KB == 8 || VB == 8) ? 1 : 2);
 }
 
 template <int KB, int VB, int G>
@@ -344,8 +344,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   const int g_own = nl - e_own * G;
   const bool col_ok = e_own < P;
   const int e_oc = col_ok ? e_own : 0;
-  const int e_row = (4 * gr) / G;  // page of the PV result rows 4*gr .. 4*gr+3 held by this lane
-  const int e_rc = e_row < P ? e_row : 0;
+  // page of the PV result row 4*gr + i held by this lane (one page for all four rows when G >= 4)
+  int e_row[4], e_rc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    e_row[i] = (4 * gr + i) / G;
+    e_rc[i] = e_row[i] < P ? e_row[i] : 0;
+  }
 
   f16x8 ONES;
 #pragma unroll
@@ -531,7 +536,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
     float arow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * gr + i);
-    const float* srow = sb + e_rc * SC;
+    const float* srow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) srow[i] = sb + e_rc[i] * SC;
 
     // PV: one accumulator per page; the lane keeps its rows' page
 #pragma unroll
@@ -545,11 +552,19 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
       }
       f32x4 dd = d[0];
 #pragma unroll
-      for (int e = 1; e < P; ++e) dd = (e_row == e) ? d[e] : dd;
-      dd = mfma16(afake, BFAKE, dd);
-      const float cv = srow[3 * 128 + 16 * nb + nl];
+      for (int e = 1; e < P; ++e)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv * dd[i]);
+        for (int i = 0; i < 4; ++i) dd[i] = (e_row[i] == e) ? d[e][i] : dd[i];
+      dd = mfma16(afake, BFAKE, dd);
+      float cv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cv[i] = (G >= 4 || i == 0) ? srow[i][3 * 128 + 16 * nb + nl] : cv[0];
+      if constexpr (G < 4) {
+#pragma unroll
+        for (int i = 1; i < 4; ++i) cv[i] = srow[i][3 * 128 + 16 * nb + nl];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv[i] * dd[i]);
     }
     // the next group's K codes of blocks 0-3 and its scales, in flight while the next step starts
     __builtin_amdgcn_sched_barrier(0);
@@ -747,8 +762,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
 }
 
 int decode_pages_per_step(int kb, int vb, int group_size) {
-  if (group_size == 8) return (kb == 8 || vb == 8) ? 1 : 2;
-  return 1;
+  if (group_size >= 16) return 1;
+  return (kb == 8 || vb == 8) ? 1 : 2;
 }
 
 DecodePlan plan_decode(int kb, int vb, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq) {
@@ -768,7 +783,8 @@ DecodePlan plan_decode(int kb, int vb, int num_seqs, int num_kv_heads, int group
 }
 
 bool decode_supported(int kb, int vb, int group_size) {
-  return (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8) && (group_size == 8 || group_size == 16);
+  return (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8) &&
+         (group_size == 1 || group_size == 2 || group_size == 4 || group_size == 8 || group_size == 16);
 }
 
 template <int KB, int VB, int G>
@@ -797,6 +813,33 @@ hipError_t launch_decode(int kb, int vb, int group_size, const _Float16* q, cons
   if (kb == KB_ && vb == VB_ && group_size == G_)                                                                \
     return launch_decode_t<KB_, VB_, G_>(q, cache, page_stride, page_table, max_pages, seq_lens, tail_k, tail_v, \
                                          sm_scale, out, workspace, num_seqs, num_q_heads, num_kv_heads, plan, stream);
+  KVARN_DECODE_CASE(2, 2, 1)
+  KVARN_DECODE_CASE(2, 4, 1)
+  KVARN_DECODE_CASE(2, 8, 1)
+  KVARN_DECODE_CASE(4, 2, 1)
+  KVARN_DECODE_CASE(4, 4, 1)
+  KVARN_DECODE_CASE(4, 8, 1)
+  KVARN_DECODE_CASE(8, 2, 1)
+  KVARN_DECODE_CASE(8, 4, 1)
+  KVARN_DECODE_CASE(8, 8, 1)
+  KVARN_DECODE_CASE(2, 2, 2)
+  KVARN_DECODE_CASE(2, 4, 2)
+  KVARN_DECODE_CASE(2, 8, 2)
+  KVARN_DECODE_CASE(4, 2, 2)
+  KVARN_DECODE_CASE(4, 4, 2)
+  KVARN_DECODE_CASE(4, 8, 2)
+  KVARN_DECODE_CASE(8, 2, 2)
+  KVARN_DECODE_CASE(8, 4, 2)
+  KVARN_DECODE_CASE(8, 8, 2)
+  KVARN_DECODE_CASE(2, 2, 4)
+  KVARN_DECODE_CASE(2, 4, 4)
+  KVARN_DECODE_CASE(2, 8, 4)
+  KVARN_DECODE_CASE(4, 2, 4)
+  KVARN_DECODE_CASE(4, 4, 4)
+  KVARN_DECODE_CASE(4, 8, 4)
+  KVARN_DECODE_CASE(8, 2, 4)
+  KVARN_DECODE_CASE(8, 4, 4)
+  KVARN_DECODE_CASE(8, 8, 4)
   KVARN_DECODE_CASE(2, 2, 8)
   KVARN_DECODE_CASE(2, 4, 8)
   KVARN_DECODE_CASE(2, 8, 8)

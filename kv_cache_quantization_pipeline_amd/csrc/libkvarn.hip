@@ -72,7 +72,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int
       num_q_heads % num_kv_heads != 0 || max_pages_per_seq < 0)
     return 0;
   const int G = num_q_heads / num_kv_heads;
-  if (G != 8 && G != 16) return 0;
+  if (!kvarn::decode_supported(f->k_bits, f->v_bits, G)) return 0;
   const kvarn::DecodePlan plan = kvarn::plan_decode(f->k_bits, f->v_bits, num_seqs, num_kv_heads, G, max_pages_per_seq);
   return static_cast<size_t>(num_seqs) * num_q_heads * plan.n_splits * kvarn::kPartialFloats * sizeof(float);
 }

@@ -58,6 +58,8 @@ def test_record_and_workspace_sizes():
     ws = kv.decode_workspace_bytes(f, 32, 32, 4, 128)
     assert ws > 0 and ws % (132 * 4) == 0   # 132 floats per (seq, q head, split)
     assert kv.decode_workspace_bytes(f, 32, 24, 4, 128) == 0   # G = 6 unsupported
+    for G in (1, 2, 4, 8, 16):
+        assert kv.decode_workspace_bytes(f, 4, 2 * G, 2, 16) > 0
     assert kv.decode_workspace_bytes(f, 32, 30, 4, 128) == 0   # Hq % Hkv != 0
     bad = kv.Format(4, 2, 128, 64, 128, 8)
     assert kv.record_bytes(bad) == 0
@@ -99,7 +101,7 @@ def test_calls_reject_bad_arguments_before_launch():
                                         0.1, dummy, ws, wsb, None)
     assert dec(hq=15) == kv.KVARN_E_INVALID_ARG
     assert dec(hq=12, hkv=2) == kv.KVARN_E_UNSUPPORTED     # G = 6
-    assert dec(hq=8, hkv=2) == kv.KVARN_E_UNSUPPORTED      # G = 4
+    assert dec(hq=6, hkv=2) == kv.KVARN_E_UNSUPPORTED      # G = 3
     assert dec(wsb=ws_need - 1) == kv.KVARN_E_INVALID_ARG
     assert dec(ws=ctypes.c_void_p(0x1004)) == kv.KVARN_E_INVALID_ARG
     assert dec(q=None) == kv.KVARN_E_INVALID_ARG

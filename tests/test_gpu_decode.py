@@ -101,6 +101,16 @@ def test_decode_ragged_small(name, G):
     _compare(st.run_gpu(), st.run_oracle(), st.lens)
 
 
+@pytest.mark.parametrize("name", ["kvarn_k4v2_g128", "kvarn_k2v4_g128", "kvarn_k8v8_g128"])
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_decode_ragged_small_gqa(name, G):
+    """Few query heads per kv head (MHA, GQA-2, GQA-4): MFMA columns beyond the group's pages masked,
+    PV rows of one lane spanning two pages when G < 4."""
+    lens = [326, 128, 5, 0, 1, 1029, 640, 127]
+    st = Setup(name, lens, hkv=3, hq=3 * G, seed=25)
+    _compare(st.run_gpu(), st.run_oracle(), st.lens)
+
+
 def test_decode_special_values():
     st = Setup("kvarn_k4v2_g128", [1, 0, 128, 384], hkv=1, hq=8, seed=22)
     out = st.run_gpu()
