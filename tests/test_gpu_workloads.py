@@ -1,0 +1,191 @@
+"""GPU parity on the two serving-shaped workloads, at full size, through the C-ABI:
+
+* long context: 4 sequences x 131072 tokens, 8 query heads on 1 kv head (k4v2); 128 steps of
+  append-one-token + decode, the last append filling the tail and quantising it inline;
+* ragged continuous batching: 64 sequences with lengths in [1024, 32768], 32 query / 4 kv heads,
+  each sequence k4v2 or k8v8 (two pools, one decode call per format), one append + decode step;
+  the first sequence of each format is set to 127 mod 128 tokens so that its append fills a tile.
+
+Decode outputs are compared with the oracle attending over the same (GPU-written) cache bytes on
+sampled sequences; a tile quantised by the append is compared with the oracle's quantisation of the
+appended tokens."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_quantization_pipeline_amd import synth
+from parity import DECODE_REL_L2, assert_code_rate, check_record, rel_l2
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import kv_cache_quantization_pipeline_amd as kv  # noqa: E402
+
+DEV = "cuda"
+
+
+def _decode(fmt, q, cache, stride, pt, lens, tk, tv, sm, hkv):
+    B, hq = q.shape[0], q.shape[1]
+    wsb = kv.decode_workspace_bytes(fmt, B, hq, hkv, pt.shape[1])
+    ws = torch.empty(max(wsb, 16) // 4 + 4, dtype=torch.float32, device=DEV)
+    out = torch.empty(B, hq, 128, dtype=torch.float16, device=DEV)
+    kv.decode_attention(fmt, q, cache, stride, pt, lens, tk, tv, sm, out, ws, hkv)
+    return out
+
+
+def _oracle_decode(fmt, q, cache_host, stride, pt, lens, tk, tv, sm, hkv):
+    _, o64 = oracle.decode_attention(fmt.k_bits, fmt.v_bits, np.ascontiguousarray(q).view(np.uint16), cache_host,
+                                     stride, np.ascontiguousarray(pt), np.ascontiguousarray(lens, dtype=np.int32),
+                                     np.ascontiguousarray(tk).view(np.uint16), np.ascontiguousarray(tv).view(np.uint16),
+                                     sm, hkv)
+    return o64
+
+
+def _compare(gpu, ref, what):
+    for s in range(gpu.shape[0]):
+        for h in range(gpu.shape[1]):
+            e = rel_l2(gpu[s, h].astype(np.float64), ref[s, h])
+            assert e <= DECODE_REL_L2, f"{what} seq {s} head {h}: rel L2 {e:.3g}"
+
+
+def test_long_context_append_decode_steps():
+    w = synth.WORKLOADS["decode_long_b4_ctx128k"]
+    fmt = kv.format_parse("kvarn_k4v2_g128")
+    B, hq, hkv, ctx = w["batch"], w["n_q_heads"], w["n_kv_heads"], w["ctx"]
+    R = kv.record_bytes(fmt)
+    stride = hkv * R
+    full = ctx // 128
+    maxp = full + 1
+    rng = np.random.default_rng(w["seed"])
+    n_pool = B * maxp
+    pt = rng.permutation(n_pool).astype(np.int32).reshape(B, maxp)
+    # the 4 x 1024 full pages: quantised on the GPU from seeded K/V
+    k_all, v_all = synth.gen_kv(w["seed"], B * full * 128, hkv)
+    cache = torch.zeros(n_pool * stride, dtype=torch.uint8, device=DEV)
+    kv.quantize_tiles(fmt, torch.from_numpy(synth.tiles_view(k_all)).to(DEV),
+                      torch.from_numpy(synth.tiles_view(v_all)).to(DEV),
+                      torch.from_numpy(np.ascontiguousarray(pt[:, :full]).reshape(-1)).to(DEV), cache, stride)
+    del k_all, v_all
+    lens = torch.full((B,), ctx, dtype=torch.int32, device=DEV)
+    tk = torch.zeros(B, hkv, 128, 128, dtype=torch.float16, device=DEV)
+    tv = torch.zeros_like(tk)
+    q = synth.gen_q(w["seed"], B, hq)
+    qd = torch.from_numpy(q).to(DEV)
+    ptd = torch.from_numpy(pt).to(DEV)
+    sm = 1.0 / math.sqrt(128)
+    # the 128 appended tokens of every sequence, and the host mirror of the tails
+    k_new = (rng.standard_normal((128, B, hkv, 128)) * 1.5).astype(np.float16)
+    v_new = (rng.standard_normal((128, B, hkv, 128)) * 1.5).astype(np.float16)
+    h_tk = np.zeros((B, hkv, 128, 128), np.float16)
+    h_tv = np.zeros_like(h_tk)
+    checked = {0: None, 63: None, 127: None}
+    outs = {}
+    for step in range(128):
+        kv.append_token(fmt, torch.from_numpy(k_new[step]).to(DEV), torch.from_numpy(v_new[step]).to(DEV), lens,
+                        tk, tv, ptd, cache, stride)
+        out = _decode(fmt, qd, cache, stride, ptd, lens, tk, tv, sm, hkv)
+        h_tk[:, :, step] = k_new[step]
+        h_tv[:, :, step] = v_new[step]
+        if step in checked:
+            torch.cuda.synchronize()
+            outs[step] = (out.cpu().numpy(), h_tk.copy(), h_tv.copy())
+    torch.cuda.synchronize()
+    assert lens.cpu().tolist() == [ctx + 128] * B
+    host = cache.cpu().numpy()
+    # the filled tile of every sequence went to page pt[s][1024], quantised like the oracle would
+    n_bad = 0
+    for s in range(B):
+        for h in range(hkv):
+            off = int(pt[s, full]) * stride + h * R
+            rk = oracle.quantize_tile_debug(np.ascontiguousarray(k_new[:, s, h]).view(np.uint16), fmt.k_bits, 8)
+            rv = oracle.quantize_tile_debug(np.ascontiguousarray(v_new[:, s, h]).view(np.uint16), fmt.v_bits, 8)
+            n_bad += check_record(host[off:off + R], fmt.k_bits, fmt.v_bits, rk, rv, f"seq {s} filled tile")
+    assert_code_rate(n_bad, B * hkv * 2 * 128 * 128, "filled tiles")
+    # decode outputs at three steps on two sequences; the last one runs over 1025 full pages
+    seqs = [0, 3]
+    for step, (out, otk, otv) in outs.items():
+        n = step + 1
+        lens_s = np.full(len(seqs), ctx + n, np.int32)
+        tail_k = otk[seqs] if n < 128 else np.zeros_like(otk[seqs])
+        tail_v = otv[seqs] if n < 128 else np.zeros_like(otv[seqs])
+        ref = _oracle_decode(fmt, q[seqs], host, stride, pt[seqs], lens_s, tail_k, tail_v, sm, hkv)
+        _compare(out[seqs], ref, f"step {step}")
+
+
+def test_ragged_mixed_formats_step():
+    w = synth.WORKLOADS["ragged_mixed_64seq"]
+    B, hq, hkv = w["batch"], w["n_q_heads"], w["n_kv_heads"]
+    lens0 = synth.gen_lengths(w["seed"], B, w["ctx_lo"], w["ctx_hi"]).astype(np.int32)
+    fmts = synth.gen_formats(w["seed"], B)
+    names = ["kvarn_k4v2_g128", "kvarn_k8v8_g128"]
+    rng = np.random.default_rng(w["seed"])
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(w["seed"])
+    q_all = synth.gen_q(w["seed"], B, hq)
+    k_new = (rng.standard_normal((B, hkv, 128)) * 1.5).astype(np.float16)
+    v_new = (rng.standard_normal((B, hkv, 128)) * 1.5).astype(np.float16)
+    tails_k = (rng.standard_normal((B, hkv, 128, 128)) * 1.5).astype(np.float16)
+    tails_v = (rng.standard_normal((B, hkv, 128, 128)) * 1.5).astype(np.float16)
+    sm = 1.0 / math.sqrt(128)
+    for fi, name in enumerate(names):
+        idx = np.nonzero(fmts == fi)[0]
+        if len(idx) == 0:
+            continue
+        fmt = kv.format_parse(name)
+        R = kv.record_bytes(fmt)
+        stride = hkv * R
+        lens = lens0[idx].copy()
+        lens[0] = lens[0] // 128 * 128 + 127      # this sequence's append fills its tail
+        full = lens // 128
+        maxp = int(full.max()) + 2
+        n_pool = len(idx) * maxp
+        pt = rng.permutation(n_pool).astype(np.int32).reshape(len(idx), maxp)
+        cache = torch.zeros(n_pool * stride, dtype=torch.uint8, device=DEV)
+        # full pages from seeded K/V generated on the device (only the cache bytes enter the check)
+        dst = np.concatenate([pt[i, :full[i]] for i in range(len(idx))]).astype(np.int32)
+        for c0 in range(0, len(dst), 2048):
+            n = min(2048, len(dst) - c0)
+            kt = (torch.randn(n, 128, hkv, 128, generator=gen, device=DEV) * 1.5).half()
+            vt = (torch.randn(n, 128, hkv, 128, generator=gen, device=DEV) * 1.5).half()
+            kv.quantize_tiles(fmt, kt, vt, torch.from_numpy(dst[c0:c0 + n]).to(DEV), cache, stride)
+        # tails hold the len % 128 newest tokens; the append writes slot len % 128
+        tk_h = tails_k[idx].copy()
+        tv_h = tails_v[idx].copy()
+        ld = torch.from_numpy(lens.copy()).to(DEV)
+        tk = torch.from_numpy(tk_h).to(DEV)
+        tv = torch.from_numpy(tv_h).to(DEV)
+        ptd = torch.from_numpy(pt).to(DEV)
+        kv.append_token(fmt, torch.from_numpy(k_new[idx]).to(DEV), torch.from_numpy(v_new[idx]).to(DEV), ld, tk,
+                        tv, ptd, cache, stride)
+        qd = torch.from_numpy(q_all[idx]).to(DEV)
+        out = _decode(fmt, qd, cache, stride, ptd, ld, tk, tv, sm, hkv).cpu().numpy()
+        torch.cuda.synchronize()
+        new_lens = lens + 1
+        assert np.array_equal(ld.cpu().numpy(), new_lens)
+        for i in range(len(idx)):
+            tk_h[i, :, lens[i] % 128] = k_new[idx[i]]
+            tv_h[i, :, lens[i] % 128] = v_new[idx[i]]
+        host = cache.cpu().numpy()
+        # every tile the append filled went to page pt[i][len // 128], quantised like the oracle would
+        fills = [i for i in range(len(idx)) if new_lens[i] % 128 == 0]
+        assert fills
+        n_bad = 0
+        for i in fills:
+            for h in range(hkv):
+                off = int(pt[i, lens[i] // 128]) * stride + h * R
+                rk = oracle.quantize_tile_debug(tk_h[i, h].view(np.uint16), fmt.k_bits, 8)
+                rv = oracle.quantize_tile_debug(tv_h[i, h].view(np.uint16), fmt.v_bits, 8)
+                n_bad += check_record(host[off:off + R], fmt.k_bits, fmt.v_bits, rk, rv, f"{name} seq {i} filled")
+        assert_code_rate(n_bad, len(fills) * hkv * 2 * 128 * 128, f"{name} filled tiles")
+        # sampled sequences: shortest, longest, the one whose tail just filled, two more
+        pick = sorted({int(np.argmin(new_lens)), int(np.argmax(new_lens)), fills[0], 1, len(idx) // 2})
+        tail_k = tk_h[pick].copy()
+        tail_v = tv_h[pick].copy()
+        for j, i in enumerate(pick):
+            if new_lens[i] % 128 == 0:
+                tail_k[j] = 0
+                tail_v[j] = 0
+        ref = _oracle_decode(fmt, q_all[idx][pick], host, stride, pt[pick], new_lens[pick], tail_k, tail_v, sm, hkv)
+        _compare(out[pick], ref, name)
