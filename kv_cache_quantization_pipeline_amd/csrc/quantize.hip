@@ -143,8 +143,13 @@ __device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[
       inv[mb][2 * ii + 1] = v.w;
     }
   if (half == 0 && gr == 0) {
+    // c_j = sqrt(S~_j / 128) = S~_j rsq(S~_j) / sqrt(128), within 2 ulp; exactly 1 for S~_j = 128
+    // (an all-zero channel)
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) sc[16 * nb + nl] = __builtin_sqrtf(sfin[nb] * (1.0f / 128.0f));
+    for (int nb = 0; nb < 8; ++nb) {
+      const float c = sfin[nb] * __builtin_amdgcn_rsqf(sfin[nb]) * 0.08838834764831845f;
+      sc[16 * nb + nl] = sfin[nb] == 128.0f ? 1.0f : c;
+    }
   }
 
   // (W - mn) * inv as one FMA; v_cvt_pk_u8_f32 rounds it to the nearest integer (ties to even),
@@ -264,6 +269,8 @@ __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ 
   {
     f16x8 xa[4][4];
     load_x(xa, x, row_stride, last_row, half, gr, nl);
+    // all 16 loads in flight before the first MFMA waits on one
+    __builtin_amdgcn_sched_barrier(0);
     rotate(xa, R, gr, nl);
   }
   auto& A = R.y;
