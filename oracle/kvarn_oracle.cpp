@@ -35,7 +35,7 @@
 namespace {
 
 constexpr int kTok = 128;   // tokens per tile = page size [HYPHO 工程实践; 需要关注 item 3]
-constexpr int kCh = 128;    // head_dim; one quantization group of 128 channels per token
+constexpr int kCh = 128;    // head_dim; a token's channels split into 128/g quantisation groups of g
 
 // ---------------------------------------------------------------- fp16 / fp32
 
@@ -90,12 +90,16 @@ uint16_t double_to_half(double x) {
 
 struct Fmt {
   int kb, vb, iters;
+  int group;   // channels per quantisation group: 128, 64 or 32
+  int ng() const { return kCh / group; }
 };
 
 size_t k_code_bytes(const Fmt& f) { return static_cast<size_t>(kTok) * kCh * f.kb / 8; }
 size_t v_code_bytes(const Fmt& f) { return static_cast<size_t>(kTok) * kCh * f.vb / 8; }
 size_t scale_offset(const Fmt& f) { return k_code_bytes(f) + v_code_bytes(f); }
-size_t record_bytes(const Fmt& f) { return scale_offset(f) + 6 * kCh * sizeof(float); }
+// floats of one half's scales: c[128], s'[ng][128], m'[ng][128]
+size_t half_scale_floats(const Fmt& f) { return static_cast<size_t>(kCh) * (1 + 2 * f.ng()); }
+size_t record_bytes(const Fmt& f) { return scale_offset(f) + 2 * half_scale_floats(f) * sizeof(float); }
 
 // Record layout (this library's format; the pages fix none of it).
 //  K codes, token-major.  Token t owns 16*kb bytes at t*16*kb.  Unit u (0..15)
@@ -105,7 +109,10 @@ size_t record_bytes(const Fmt& f) { return scale_offset(f) + 6 * kCh * sizeof(fl
 //  ((nb*4 + gr)*16 + nl)*2U + half*U holds channel j = 16*nb + nl for the tokens
 //  t = 64*half + 16*mb + 4*gr + i (mb, i in 0..3), code of (mb, i) at bit
 //  vb*(4*mb + i).
-//  Scales: six float32[128] arrays c_K, s'_K, m'_K, c_V, s'_V, m'_V.
+//  Scales, float32, K half then V half; each half is c[128] (per channel), then
+//  s'[ng][128] and m'[ng][128] (group-major: group gi of token t at gi*128 + t),
+//  ng = 128 / g groups per token.  For g = 128 these are six float32[128] arrays
+//  c_K, s'_K, m'_K, c_V, s'_V, m'_V.
 void k_code_pos(const Fmt& f, int t, int j, size_t* byte, int* bit) {
   const int u = j % 16, e = j / 16;
   const size_t bitpos = static_cast<size_t>(t) * 16 * f.kb * 8 + static_cast<size_t>(u) * f.kb * 8 + f.kb * e;
@@ -192,20 +199,20 @@ void sinkhorn(const double* Y, int iters, double* u, double* v, double* col_dev)
   }
 }
 
-// Asymmetric round-to-nearest of one group (one token's 128 channels) at b bits
-// [HYPHO 四步流水线 第四步; LEHUY Cơ chế step 4]:  mn = min z, mx = max z,
-// s = (mx - mn) / (2^b - 1), q = clamp(rint((z - mn) / s), 0, 2^b - 1);
-// a constant group (s = 0) gets codes 0.  rint = nearest, ties to even.
-// t_out (optional) receives the unrounded (z - mn)/s.
-void rtn_group(const double* z, int bits, double* mn_out, double* s_out, uint8_t* q, double* t_out) {
+// Asymmetric round-to-nearest of one group of n values (n contiguous channels of
+// one token) at b bits [HYPHO 四步流水线 第四步; LEHUY Cơ chế step 4]:
+// mn = min z, mx = max z, s = (mx - mn) / (2^b - 1), q = clamp(rint((z - mn) / s),
+// 0, 2^b - 1); a constant group (s = 0) gets codes 0.  rint = nearest, ties to
+// even.  t_out (optional) receives the unrounded (z - mn)/s.
+void rtn_group(const double* z, int n, int bits, double* mn_out, double* s_out, uint8_t* q, double* t_out) {
   double mn = z[0], mx = z[0];
-  for (int j = 1; j < kCh; ++j) {
+  for (int j = 1; j < n; ++j) {
     mn = std::min(mn, z[j]);
     mx = std::max(mx, z[j]);
   }
   const int qmax = (1 << bits) - 1;
   const double s = (mx - mn) / qmax;
-  for (int j = 0; j < kCh; ++j) {
+  for (int j = 0; j < n; ++j) {
     if (s > 0.0) {
       const double tv = (z[j] - mn) / s;
       double r = std::nearbyint(tv);   // default rounding mode: ties to even
@@ -224,14 +231,16 @@ void rtn_group(const double* z, int bits, double* mn_out, double* s_out, uint8_t
 // Everything the tile quantizer produces for one 128x128 tile half (K or V).
 struct TileOut {
   std::vector<uint8_t> q;          // [t][j]
-  std::vector<float> c, sp, mp;    // c[j] = e^{v_j}, s'_t = e^{u_t} s_t, m'_t = e^{u_t} mn_t
+  std::vector<float> c, sp, mp;    // c[j] = e^{v_j}; [gi][t]: s' = e^{u_t} s_{t,gi}, m' = e^{u_t} mn_{t,gi}
   std::vector<double> y, u, v, z, tval, col_dev;
 };
 
-// Steps 1-5 on one tile half: upcast, rotate, normalise, quantise, scales.
+// Steps 1-5 on one tile half: upcast, rotate, normalise, quantise (groups of
+// `group` contiguous channels of each token), scales.
 // x16: fp16 bits, token t at x16 + t*row_stride, 128 channels contiguous.
-void quantize_tile_half(const uint16_t* x16, int64_t row_stride, int bits, int iters, TileOut* o,
+void quantize_tile_half(const uint16_t* x16, int64_t row_stride, int bits, int iters, int group, TileOut* o,
                         bool debug) {
+  const int ng = kCh / group;
   std::vector<double> x(kTok * kCh), y(kTok * kCh), z(kTok * kCh), tval(kTok * kCh);
   for (int t = 0; t < kTok; ++t)
     for (int j = 0; j < kCh; ++j) x[t * kCh + j] = half_to_double(x16[t * row_stride + j]);
@@ -242,14 +251,17 @@ void quantize_tile_half(const uint16_t* x16, int64_t row_stride, int bits, int i
     for (int j = 0; j < kCh; ++j) z[t * kCh + j] = y[t * kCh + j] * std::exp(-u[t] - v[j]);
   o->q.assign(kTok * kCh, 0);
   o->c.assign(kCh, 0.f);
-  o->sp.assign(kTok, 0.f);
-  o->mp.assign(kTok, 0.f);
+  o->sp.assign(static_cast<size_t>(ng) * kTok, 0.f);
+  o->mp.assign(static_cast<size_t>(ng) * kTok, 0.f);
   for (int t = 0; t < kTok; ++t) {
-    double mn, s;
-    rtn_group(&z[t * kCh], bits, &mn, &s, &o->q[t * kCh], &tval[t * kCh]);
     const double r = std::exp(u[t]);
-    o->sp[t] = static_cast<float>(r * s);
-    o->mp[t] = static_cast<float>(r * mn);
+    for (int gi = 0; gi < ng; ++gi) {
+      const int j0 = gi * group;
+      double mn, s;
+      rtn_group(&z[t * kCh + j0], group, bits, &mn, &s, &o->q[t * kCh + j0], &tval[t * kCh + j0]);
+      o->sp[gi * kTok + t] = static_cast<float>(r * s);
+      o->mp[gi * kTok + t] = static_cast<float>(r * mn);
+    }
   }
   for (int j = 0; j < kCh; ++j) o->c[j] = static_cast<float>(std::exp(v[j]));
   if (debug) {
@@ -284,17 +296,19 @@ void pack_record(const Fmt& f, const TileOut& K, const TileOut& V, uint8_t* rec)
       put_code(rec, byte, bit, f.vb, V.q[t * kCh + j]);
     }
   float* sc = reinterpret_cast<float*>(rec + scale_offset(f));
-  for (int i = 0; i < kCh; ++i) {
-    sc[0 * kCh + i] = K.c[i];
-    sc[1 * kCh + i] = K.sp[i];
-    sc[2 * kCh + i] = K.mp[i];
-    sc[3 * kCh + i] = V.c[i];
-    sc[4 * kCh + i] = V.sp[i];
-    sc[5 * kCh + i] = V.mp[i];
+  const int ng = f.ng();
+  const TileOut* half[2] = {&K, &V};
+  for (int hv = 0; hv < 2; ++hv) {
+    float* h = sc + hv * half_scale_floats(f);
+    for (int i = 0; i < kCh; ++i) h[i] = half[hv]->c[i];
+    for (int i = 0; i < ng * kTok; ++i) {
+      h[kCh + i] = half[hv]->sp[i];
+      h[kCh + ng * kTok + i] = half[hv]->mp[i];
+    }
   }
 }
 
-// Read a record back: codes [t][j] and the six scale arrays.
+// Read a record back: codes [t][j] and the scale block (2 * half_scale_floats).
 void unpack_record(const Fmt& f, const uint8_t* rec, uint8_t* qk, uint8_t* qv, float* scales) {
   for (int t = 0; t < kTok; ++t)
     for (int j = 0; j < kCh; ++j) {
@@ -305,27 +319,31 @@ void unpack_record(const Fmt& f, const uint8_t* rec, uint8_t* qk, uint8_t* qv, f
       v_code_pos(f, t, j, &byte, &bit);
       qv[t * kCh + j] = get_code(rec, byte, bit, f.vb);
     }
-  std::memcpy(scales, rec + scale_offset(f), 6 * kCh * sizeof(float));
+  std::memcpy(scales, rec + scale_offset(f), 2 * half_scale_floats(f) * sizeof(float));
 }
 
-// Reconstruction of one half: yhat_t = c ⊙ (m'_t + s'_t q_t) in the rotated
-// domain, then xhat_t = Hn yhat_t (Hn is its own inverse)  [HYPHO 四步流水线
-// 第四步: scales are restored on read].
-void dequant_half(const uint8_t* q, const float* c, const float* sp, const float* mp, double* xhat) {
+// Reconstruction of one half: yhat_tj = c_j (m'_{t,g(j)} + s'_{t,g(j)} q_tj) in
+// the rotated domain (g(j) = j / group), then xhat_t = Hn yhat_t (Hn is its own
+// inverse)  [HYPHO 四步流水线 第四步: scales are restored on read].
+void dequant_half(const uint8_t* q, const float* c, const float* sp, const float* mp, int group, double* xhat) {
   std::vector<double> yhat(kTok * kCh);
   for (int t = 0; t < kTok; ++t)
-    for (int j = 0; j < kCh; ++j)
-      yhat[t * kCh + j] = static_cast<double>(c[j]) *
-                          (static_cast<double>(mp[t]) + static_cast<double>(sp[t]) * q[t * kCh + j]);
+    for (int j = 0; j < kCh; ++j) {
+      const int gi = j / group;
+      yhat[t * kCh + j] = static_cast<double>(c[j]) * (static_cast<double>(mp[gi * kTok + t]) +
+                                                      static_cast<double>(sp[gi * kTok + t]) * q[t * kCh + j]);
+    }
   rotate_rows(yhat.data(), xhat, kTok);
 }
 
 void dequant_record(const Fmt& f, const uint8_t* rec, double* khat, double* vhat) {
   std::vector<uint8_t> qk(kTok * kCh), qv(kTok * kCh);
-  std::vector<float> sc(6 * kCh);
+  const size_t hs = half_scale_floats(f);
+  const int ng = f.ng();
+  std::vector<float> sc(2 * hs);
   unpack_record(f, rec, qk.data(), qv.data(), sc.data());
-  dequant_half(qk.data(), &sc[0], &sc[kCh], &sc[2 * kCh], khat);
-  dequant_half(qv.data(), &sc[3 * kCh], &sc[4 * kCh], &sc[5 * kCh], vhat);
+  dequant_half(qk.data(), &sc[0], &sc[kCh], &sc[kCh + ng * kTok], f.group, khat);
+  dequant_half(qv.data(), &sc[hs], &sc[hs + kCh], &sc[hs + kCh + ng * kTok], f.group, vhat);
 }
 
 void parallel_for(int64_t n, int nthreads, const std::function<void(int64_t)>& fn) {
@@ -343,9 +361,9 @@ void parallel_for(int64_t n, int nthreads, const std::function<void(int64_t)>& f
   for (auto& th : pool) th.join();
 }
 
-bool fmt_ok(int kb, int vb, int iters) {
+bool fmt_ok(int kb, int vb, int iters, int group) {
   auto ok = [](int b) { return b == 2 || b == 4 || b == 8; };
-  return ok(kb) && ok(vb) && iters >= 0;
+  return ok(kb) && ok(vb) && iters >= 0 && (group == 32 || group == 64 || group == 128);
 }
 
 }  // namespace
@@ -356,7 +374,7 @@ int oracle_threads_used(int requested) {
   return requested > 0 ? requested : static_cast<int>(std::max(1u, std::thread::hardware_concurrency()));
 }
 
-size_t oracle_record_bytes(int kb, int vb) { return record_bytes(Fmt{kb, vb, 0}); }
+size_t oracle_record_bytes(int kb, int vb, int group) { return record_bytes(Fmt{kb, vb, 0, group}); }
 
 // fp16 helpers (pinned against numpy's float16 conversion).
 void oracle_half_to_double(const uint16_t* h, double* d, int64_t n) {
@@ -375,21 +393,22 @@ void oracle_sinkhorn(const double* y, int iters, double* u, double* v, double* c
   sinkhorn(y, iters, u, v, col_dev);
 }
 
-// RTN of `rows` groups of 128 (pinned: brute-force nearest level, error <= s/2).
-void oracle_rtn(const double* z, int rows, int bits, double* mn, double* s, uint8_t* q, double* tval) {
+// RTN of `rows` groups of n values (pinned: brute-force nearest level, error <= s/2).
+void oracle_rtn(const double* z, int rows, int n, int bits, double* mn, double* s, uint8_t* q, double* tval) {
   for (int r = 0; r < rows; ++r)
-    rtn_group(z + r * kCh, bits, &mn[r], &s[r], q + r * kCh, tval ? tval + r * kCh : nullptr);
+    rtn_group(z + static_cast<int64_t>(r) * n, n, bits, &mn[r], &s[r], q + static_cast<int64_t>(r) * n,
+              tval ? tval + static_cast<int64_t>(r) * n : nullptr);
 }
 
 // Full tile-half pipeline with every intermediate exposed (fp64 where the method
 // computes, fp32 where it stores): y, u, v, z, tval [t][j] = (z - mn)/s before
-// rounding, codes q, scales c/s'/m', col_dev[iters].
-int oracle_quantize_tile_debug(const uint16_t* x16, int bits, int iters, double* y, double* u, double* v,
-                               double* z, double* tval, uint8_t* q, float* c, float* sp, float* mp,
+// rounding, codes q, scales c[128], s'/m' [128/group][128], col_dev[iters].
+int oracle_quantize_tile_debug(const uint16_t* x16, int bits, int iters, int group, double* y, double* u,
+                               double* v, double* z, double* tval, uint8_t* q, float* c, float* sp, float* mp,
                                double* col_dev) {
-  if (!(bits == 2 || bits == 4 || bits == 8) || iters < 0) return 1;
+  if (!fmt_ok(bits, bits, iters, group)) return 1;
   TileOut o;
-  quantize_tile_half(x16, kCh, bits, iters, &o, true);
+  quantize_tile_half(x16, kCh, bits, iters, group, &o, true);
   std::memcpy(y, o.y.data(), sizeof(double) * kTok * kCh);
   std::memcpy(u, o.u.data(), sizeof(double) * kTok);
   std::memcpy(v, o.v.data(), sizeof(double) * kCh);
@@ -397,49 +416,53 @@ int oracle_quantize_tile_debug(const uint16_t* x16, int bits, int iters, double*
   std::memcpy(tval, o.tval.data(), sizeof(double) * kTok * kCh);
   std::memcpy(q, o.q.data(), kTok * kCh);
   std::memcpy(c, o.c.data(), sizeof(float) * kCh);
-  std::memcpy(sp, o.sp.data(), sizeof(float) * kTok);
-  std::memcpy(mp, o.mp.data(), sizeof(float) * kTok);
+  std::memcpy(sp, o.sp.data(), sizeof(float) * o.sp.size());
+  std::memcpy(mp, o.mp.data(), sizeof(float) * o.mp.size());
   if (col_dev && iters > 0) std::memcpy(col_dev, o.col_dev.data(), sizeof(double) * iters);
   return 0;
 }
 
-// Pack / unpack one record from / to codes [t][j] and six scale arrays.
-int oracle_pack_record(int kb, int vb, const uint8_t* qk, const uint8_t* qv, const float* scales,
+// Pack / unpack one record from / to codes [t][j] and the scale block (K half
+// c, s'[ng], m'[ng], then the V half; 2 * 128 * (1 + 2 ng) floats).
+int oracle_pack_record(int kb, int vb, int group, const uint8_t* qk, const uint8_t* qv, const float* scales,
                        uint8_t* rec) {
-  if (!fmt_ok(kb, vb, 0)) return 1;
-  Fmt f{kb, vb, 0};
+  if (!fmt_ok(kb, vb, 0, group)) return 1;
+  const Fmt f{kb, vb, 0, group};
+  const size_t hs = half_scale_floats(f);
+  const int ng = f.ng();
   TileOut K, V;
   K.q.assign(qk, qk + kTok * kCh);
   V.q.assign(qv, qv + kTok * kCh);
-  K.c.assign(scales, scales + kCh);
-  K.sp.assign(scales + kCh, scales + 2 * kCh);
-  K.mp.assign(scales + 2 * kCh, scales + 3 * kCh);
-  V.c.assign(scales + 3 * kCh, scales + 4 * kCh);
-  V.sp.assign(scales + 4 * kCh, scales + 5 * kCh);
-  V.mp.assign(scales + 5 * kCh, scales + 6 * kCh);
+  TileOut* half[2] = {&K, &V};
+  for (int hv = 0; hv < 2; ++hv) {
+    const float* h = scales + hv * hs;
+    half[hv]->c.assign(h, h + kCh);
+    half[hv]->sp.assign(h + kCh, h + kCh + ng * kTok);
+    half[hv]->mp.assign(h + kCh + ng * kTok, h + kCh + 2 * ng * kTok);
+  }
   pack_record(f, K, V, rec);
   return 0;
 }
-int oracle_unpack_record(int kb, int vb, const uint8_t* rec, uint8_t* qk, uint8_t* qv, float* scales) {
-  if (!fmt_ok(kb, vb, 0)) return 1;
-  unpack_record(Fmt{kb, vb, 0}, rec, qk, qv, scales);
+int oracle_unpack_record(int kb, int vb, int group, const uint8_t* rec, uint8_t* qk, uint8_t* qv, float* scales) {
+  if (!fmt_ok(kb, vb, 0, group)) return 1;
+  unpack_record(Fmt{kb, vb, 0, group}, rec, qk, qv, scales);
   return 0;
 }
 
 // Dequantised K and V of one record, raw (unrotated) domain, fp64 [t][j].
-int oracle_dequant_record(int kb, int vb, const uint8_t* rec, double* khat, double* vhat) {
-  if (!fmt_ok(kb, vb, 0)) return 1;
-  dequant_record(Fmt{kb, vb, 0}, rec, khat, vhat);
+int oracle_dequant_record(int kb, int vb, int group, const uint8_t* rec, double* khat, double* vhat) {
+  if (!fmt_ok(kb, vb, 0, group)) return 1;
+  dequant_record(Fmt{kb, vb, 0, group}, rec, khat, vhat);
   return 0;
 }
 
 // Bulk quantise: k, v fp16 [num_tiles][128][num_kv_heads][128]; tile i of head h
 // goes to cache + dst_pages[i]*page_stride + h*record_bytes.
-int oracle_quantize_tiles(int kb, int vb, int iters, int num_tiles, int num_kv_heads, const uint16_t* k,
+int oracle_quantize_tiles(int kb, int vb, int iters, int group, int num_tiles, int num_kv_heads, const uint16_t* k,
                           const uint16_t* v, const int32_t* dst_pages, uint8_t* cache, int64_t page_stride,
                           int nthreads) {
-  if (!fmt_ok(kb, vb, iters) || num_tiles < 0 || num_kv_heads <= 0) return 1;
-  const Fmt f{kb, vb, iters};
+  if (!fmt_ok(kb, vb, iters, group) || num_tiles < 0 || num_kv_heads <= 0) return 1;
+  const Fmt f{kb, vb, iters, group};
   const size_t R = record_bytes(f);
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * kCh;
   parallel_for(static_cast<int64_t>(num_tiles) * num_kv_heads, nthreads, [&](int64_t w) {
@@ -447,8 +470,8 @@ int oracle_quantize_tiles(int kb, int vb, int iters, int num_tiles, int num_kv_h
     const int h = static_cast<int>(w % num_kv_heads);
     const int64_t base = tile * kTok * row_stride + static_cast<int64_t>(h) * kCh;
     TileOut K, V;
-    quantize_tile_half(k + base, row_stride, kb, iters, &K, false);
-    quantize_tile_half(v + base, row_stride, vb, iters, &V, false);
+    quantize_tile_half(k + base, row_stride, kb, iters, group, &K, false);
+    quantize_tile_half(v + base, row_stride, vb, iters, group, &V, false);
     pack_record(f, K, V, cache + dst_pages[tile] * page_stride + static_cast<int64_t>(h) * R);
   });
   return 0;
@@ -457,12 +480,12 @@ int oracle_quantize_tiles(int kb, int vb, int iters, int num_tiles, int num_kv_h
 // Append one token per sequence (step 7 of the reading): the token goes, raw
 // fp16, into tail[s][h][len % 128]; len += 1; when len % 128 == 0 the tail tile
 // is quantised into page page_table[s][len/128 - 1].
-int oracle_append_token(int kb, int vb, int iters, int num_seqs, int num_kv_heads, const uint16_t* k_new,
+int oracle_append_token(int kb, int vb, int iters, int group, int num_seqs, int num_kv_heads, const uint16_t* k_new,
                         const uint16_t* v_new, int32_t* seq_lens, uint16_t* tail_k, uint16_t* tail_v,
                         const int32_t* page_table, int max_pages_per_seq, uint8_t* cache, int64_t page_stride,
                         int nthreads) {
-  if (!fmt_ok(kb, vb, iters) || num_seqs < 0 || num_kv_heads <= 0) return 1;
-  const Fmt f{kb, vb, iters};
+  if (!fmt_ok(kb, vb, iters, group) || num_seqs < 0 || num_kv_heads <= 0) return 1;
+  const Fmt f{kb, vb, iters, group};
   const size_t R = record_bytes(f);
   parallel_for(num_seqs, nthreads, [&](int64_t s) {
     const int len = seq_lens[s];
@@ -477,8 +500,8 @@ int oracle_append_token(int kb, int vb, int iters, int num_seqs, int num_kv_head
       if ((len + 1) % kTok == 0) {
         const int page = page_table[s * max_pages_per_seq + len / kTok];
         TileOut K, V;
-        quantize_tile_half(tail_k + tbase, kCh, kb, iters, &K, false);
-        quantize_tile_half(tail_v + tbase, kCh, vb, iters, &V, false);
+        quantize_tile_half(tail_k + tbase, kCh, kb, iters, group, &K, false);
+        quantize_tile_half(tail_v + tbase, kCh, vb, iters, group, &V, false);
         pack_record(f, K, V, cache + page * page_stride + static_cast<int64_t>(h) * R);
       }
     }
@@ -492,13 +515,13 @@ int oracle_append_token(int kb, int vb, int iters, int num_seqs, int num_kv_head
 // are dequantised and inverse-rotated, tail tokens are the raw fp16 rows, then
 // out = softmax(sm_scale * q.K^T) V in fp64, rounded to fp16.  L = 0 -> zeros.
 // Each decode step reads every cached token [HYPHO 论文的核心发现].
-int oracle_decode_attention(int kb, int vb, int num_seqs, int num_q_heads, int num_kv_heads, const uint16_t* q,
-                            const uint8_t* cache, int64_t page_stride, const int32_t* page_table,
+int oracle_decode_attention(int kb, int vb, int group, int num_seqs, int num_q_heads, int num_kv_heads,
+                            const uint16_t* q, const uint8_t* cache, int64_t page_stride, const int32_t* page_table,
                             int max_pages_per_seq, const int32_t* seq_lens, const uint16_t* tail_k,
                             const uint16_t* tail_v, double sm_scale, uint16_t* out, double* out_f64,
                             int nthreads) {
-  if (!fmt_ok(kb, vb, 0) || num_seqs < 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 1;
-  const Fmt f{kb, vb, 0};
+  if (!fmt_ok(kb, vb, 0, group) || num_seqs < 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 1;
+  const Fmt f{kb, vb, 0, group};
   const size_t R = record_bytes(f);
   const int G = num_q_heads / num_kv_heads;
   parallel_for(static_cast<int64_t>(num_seqs) * num_kv_heads, nthreads, [&](int64_t w) {

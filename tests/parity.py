@@ -23,7 +23,8 @@ DECODE_REL_L2 = 2e-3
 
 
 def check_half(q_gpu, c_gpu, sp_gpu, mp_gpu, ref, bits, what=""):
-    """Compare one tile half (codes [128,128], scales) with oracle.quantize_tile_debug output."""
+    """Compare one tile half (codes [128,128], scales) with oracle.quantize_tile_debug output.
+    s' and m' are [128] (one group per token) or [ng][128] (groups of 128/ng channels)."""
     qmax = (1 << bits) - 1
     c_ref, sp_ref, mp_ref = ref["c"], ref["sp"], ref["mp"]
     rc = np.abs(c_gpu.astype(np.float64) - c_ref) / np.abs(c_ref)
@@ -51,14 +52,15 @@ def assert_code_rate(n_bad, n_codes, what=""):
     assert n_bad <= CODE_MISMATCH_RATE * n_codes, f"{what} {n_bad} code mismatches in {n_codes}"
 
 
-def check_record(rec_gpu, kb, vb, ref_k, ref_v, what=""):
+def check_record(rec_gpu, kb, vb, ref_k, ref_v, what="", group=128):
     """Full record check: layout bit-exact, K and V halves within tolerance.  Returns the number of
     code mismatches (each already checked to be a +-1 flip at a near tie)."""
     # Codes are read out of the GPU bytes at the positions the oracle's layout defines, so a
     # misplaced bit shows up as mismatches far beyond the tie criterion below.
-    qk, qv, sc = oracle.unpack_record(kb, vb, rec_gpu)
-    nk = check_half(qk, sc[0], sc[1], sc[2], ref_k, kb, what + " K")
-    nv = check_half(qv, sc[3], sc[4], sc[5], ref_v, vb, what + " V")
+    qk, qv, sc = oracle.unpack_record(kb, vb, rec_gpu, group)
+    ck, spk, mpk, cv, spv, mpv = oracle.split_scales(sc, group)
+    nk = check_half(qk, ck, spk, mpk, ref_k, kb, what + " K")
+    nv = check_half(qv, cv, spv, mpv, ref_v, vb, what + " V")
     return nk + nv
 
 

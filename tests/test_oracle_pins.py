@@ -379,3 +379,121 @@ def test_decode_special_cases():
     a, _ = oracle.decode_attention(4, 2, qr, cache, R, pt, np.array([130], np.int32), tk, tv, 0.1, 1)
     b, _ = oracle.decode_attention(4, 2, qr, cache2, R, pt2, np.array([130], np.int32), tk, tv, 0.1, 1)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------- quantisation groups below 128 channels
+# "g64" / "g32": each token's 128 rotated, normalised channels are cut into contiguous groups of
+# 64 / 32 channels, each with its own (mn, s); the rotation and the normalisation do not change.
+
+@pytest.mark.parametrize("group", [32, 64])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_grouped_rtn_is_per_group_nearest_level_brute_force(group, bits):
+    kx, _ = _single_tile_inputs()
+    full = oracle.quantize_tile_debug(kx, bits, 8)
+    o = oracle.quantize_tile_debug(kx, bits, 8, group=group)
+    for key in ("y", "u", "v", "z", "c"):
+        assert np.array_equal(o[key], full[key]), key       # normalisation independent of the group
+    ng, qmax = 128 // group, (1 << bits) - 1
+    z, u, q = o["z"], o["u"], o["q"]
+    assert o["sp"].shape == (ng, 128) and o["mp"].shape == (ng, 128)
+    n_checked = 0
+    for gi in range(ng):
+        zg = z[:, gi * group:(gi + 1) * group]
+        mn, mx = zg.min(axis=1), zg.max(axis=1)
+        s = (mx - mn) / qmax
+        qg = q[:, gi * group:(gi + 1) * group].astype(np.int64)
+        assert np.all(qg[np.arange(128), zg.argmin(axis=1)] == 0)
+        assert np.all(qg[np.arange(128), zg.argmax(axis=1)] == qmax)
+        levels = mn[:, None, None] + s[:, None, None] * np.arange(qmax + 1)[None, None, :]
+        best = np.abs(levels - zg[:, :, None]).argmin(axis=2)
+        tv = (zg - mn[:, None]) / s[:, None]
+        not_tie = np.abs(tv - np.floor(tv) - 0.5) > 1e-9
+        assert np.array_equal(best[not_tie], qg[not_tie])
+        n_checked += int(not_tie.sum())
+        np.testing.assert_array_equal(o["sp"][gi], (np.exp(u) * s).astype(np.float32))
+        np.testing.assert_array_equal(o["mp"][gi], (np.exp(u) * mn).astype(np.float32))
+    assert n_checked > 0.99 * 128 * 128
+    # a finer group never has a wider range than the whole token
+    assert np.all(o["sp"] <= full["sp"][None, :] * (1 + 1e-6))
+
+
+def test_grouped_record_sizes_and_scale_layout():
+    # codes as in the g128 layout; the scale block is, per half, c[128], s'[ng][128], m'[ng][128]
+    assert oracle.record_bytes(4, 2, 64) == 12288 + 2 * 4 * 128 * 5 == 17408
+    assert oracle.record_bytes(4, 2, 32) == 12288 + 2 * 4 * 128 * 9 == 21504
+    assert oracle.record_bytes(8, 8, 32) == 32768 + 9216
+    rng = np.random.default_rng(31)
+    qk = rng.integers(0, 16, (128, 128)).astype(np.uint8)
+    qv = rng.integers(0, 4, (128, 128)).astype(np.uint8)
+    for group in (64, 32):
+        ng = 128 // group
+        scales = np.arange(2 * (1 + 2 * ng) * 128, dtype=np.float32).reshape(-1, 128)
+        rec = oracle.pack_record(4, 2, qk, qv, scales, group=group)
+        ref = oracle.pack_record(4, 2, qk, qv, np.zeros((6, 128), np.float32))
+        assert np.array_equal(rec[:12288], ref[:12288])
+        sc = rec[12288:].view(np.float32)
+        # hand-derived offsets (floats): K half at 0, V half at 128 (1 + 2 ng); s'_gi at 128 + 128 gi,
+        # m'_gi at 128 (1 + ng) + 128 gi; group gi of token t at + t
+        hs = 128 * (1 + 2 * ng)
+        for hv in range(2):
+            for gi in range(ng):
+                t = 77
+                assert sc[hv * hs + 128 + 128 * gi + t] == scales[hv * (1 + 2 * ng) + 1 + gi, t]
+                assert sc[hv * hs + 128 * (1 + ng) + 128 * gi + t] == scales[hv * (1 + 2 * ng) + 1 + ng + gi, t]
+        qk2, qv2, sc2 = oracle.unpack_record(4, 2, rec, group)
+        assert np.array_equal(qk2, qk) and np.array_equal(qv2, qv) and np.array_equal(sc2, scales)
+        ck, spk, mpk, cv, spv, mpv = oracle.split_scales(sc2, group)
+        assert np.array_equal(spk[ng - 1], scales[ng]) and np.array_equal(mpv[0], scales[(1 + 2 * ng) + 1 + ng])
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_grouped_dequant_error_is_within_half_a_step_of_its_group(group):
+    # Rotated-domain reconstruction yhat = khat Hn must be within c_j s'_{t,g(j)} / 2 of Y: a
+    # dequantiser that used another group's (s', m') breaks this bound.
+    kx, vx = _single_tile_inputs()
+    kt = kx.reshape(1, 128, 1, 128)
+    vt = vx.reshape(1, 128, 1, 128)
+    R = oracle.record_bytes(4, 2, group)
+    cache = np.zeros(R, np.uint8)
+    oracle.quantize_tiles(4, 2, 8, kt, vt, np.array([0], np.int32), cache, R, group=group)
+    khat, vhat = oracle.dequant_record(4, 2, cache, group)
+    Hn = scipy.linalg.hadamard(128) / math.sqrt(128)
+    errs = []
+    for half, xhat, bits in (("k", khat, 4), ("v", vhat, 2)):
+        o = oracle.quantize_tile_debug(kx if half == "k" else vx, bits, 8, group=group)
+        yhat = xhat @ Hn
+        sp = o["sp"].reshape(-1, 128)                         # [ng][t]
+        step = o["c"][None, :].astype(np.float64) * np.repeat(sp.T, group, axis=1)   # [t][j]
+        err = np.abs(yhat - o["y"])
+        assert np.all(err <= step / 2 * (1 + 1e-5) + 1e-9), (half, float((err - step / 2).max()))
+        errs.append(err.mean())
+    if group < 128:
+        R128 = oracle.record_bytes(4, 2)
+        c128 = np.zeros(R128, np.uint8)
+        oracle.quantize_tiles(4, 2, 8, kt, vt, np.array([0], np.int32), c128, R128)
+        k128, _ = oracle.dequant_record(4, 2, c128)
+        x = kx.view(np.float16).astype(np.float64)
+        assert np.abs(khat - x).mean() < np.abs(k128 - x).mean()
+
+
+def test_grouped_decode_is_attention_over_the_grouped_dequantisation():
+    kt, vt = _small_workload(seed=12, n_tiles=2, hkv=1)
+    for group in (32, 64):
+        R = oracle.record_bytes(4, 2, group)
+        cache = np.zeros(2 * R, np.uint8)
+        oracle.quantize_tiles(4, 2, 8, kt, vt, np.array([1, 0], np.int32), cache, R, group=group)
+        rng = np.random.default_rng(13)
+        q = rng.standard_normal((1, 4, 128)).astype(np.float16)
+        tk = (rng.standard_normal((1, 1, 128, 128))).astype(np.float16)
+        tv = (rng.standard_normal((1, 1, 128, 128))).astype(np.float16)
+        lens = np.array([256 + 9], np.int32)
+        pt = np.array([[1, 0, 0]], np.int32)
+        _, o = oracle.decode_attention(4, 2, q.view(np.uint16), cache, R, pt, lens, tk.view(np.uint16),
+                                       tv.view(np.uint16), 0.09, 1, group=group)
+        k1, v1 = oracle.dequant_record(4, 2, cache[R:2 * R], group)
+        k0, v0 = oracle.dequant_record(4, 2, cache[:R], group)
+        K = np.concatenate([k1, k0, tk[0, 0, :9].astype(np.float64)])
+        V = np.concatenate([v1, v0, tv[0, 0, :9].astype(np.float64)])
+        for h in range(4):
+            ref = _attend_np(q[0, h].astype(np.float64), K, V, 0.09)
+            np.testing.assert_allclose(o[0, h], ref, rtol=1e-10, atol=1e-12)
