@@ -1,31 +1,55 @@
 """Compile the HIP sources of libkvarn for gfx950 into an in-tree shared library.
 
-hipcc, -O3, packed fp32 instructions disabled for device code.  The library is
-written next to this file as libkvarn.so and loaded by the binding.
+hipcc, -O3, packed fp32 instructions disabled for device code.  Each translation unit is compiled
+to an object in parallel (decode.hip once per number of quantisation groups per token), then the
+objects are linked.  The library is written next to this file as libkvarn.so and loaded by the
+binding.
 """
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvarn.so")
-SOURCES = ["libkvarn.hip", "quantize.hip", "decode.hip"]
 ARCH = "gfx950"
+# (source, extra defines, object name)
+UNITS = [
+    ("libkvarn.hip", [], "libkvarn.o"),
+    ("quantize.hip", [], "quantize.o"),
+    ("decode.hip", ["-DKVARN_DECODE_NG=1"], "decode_ng1.o"),
+    ("decode.hip", ["-DKVARN_DECODE_NG=2"], "decode_ng2.o"),
+    ("decode.hip", ["-DKVARN_DECODE_NG=4"], "decode_ng4.o"),
+]
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    cmd = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"),
-           "-o", LIB + ".tmp"] + list(extra) + [os.path.join(CSRC, s) for s in SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libkvarn")
+        raise RuntimeError("hipcc failed: " + " ".join(cmd[-3:]))
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    with tempfile.TemporaryDirectory(prefix="kvarn_build_") as tmp:
+        jobs = []
+        for src, defs, obj in UNITS:
+            jobs.append(["hipcc", "-c"] + FLAGS + list(extra) + defs +
+                        ["-o", os.path.join(tmp, obj), os.path.join(CSRC, src)])
+        workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            for f in [ex.submit(_run, j, verbose) for j in jobs]:
+                f.result()
+        _run(["hipcc", "-shared", f"--offload-arch={ARCH}", "-o", LIB + ".tmp"] +
+             [os.path.join(tmp, obj) for _, _, obj in UNITS], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -30,6 +30,13 @@
 #include "kvarn_device.h"
 #include "kvarn_internal.h"
 
+// This file is compiled once per number of quantisation groups per token: KVARN_DECODE_NG = 1 (the
+// default; also holds the host-side planning and dispatch), 2 or 4.  Each object holds the kernels
+// of its group count, with internal linkage, and one launcher for them.
+#ifndef KVARN_DECODE_NG
+#define KVARN_DECODE_NG 1
+#endif
+
 namespace kvarn {
 
 namespace {
@@ -108,6 +115,44 @@ __device__ __forceinline__ f16x8 dequant_k(const KRegs<KB>& r, int kb) {
   } else {
     const uint32_t d0 = r.w[kb >> 1][2 * (kb & 1)], d1 = r.w[kb >> 1][2 * (kb & 1) + 1];
     return cat4(u8pair_to_f16(d0), u8pair_to_f16(d0 >> 8), u8pair_to_f16(d1), u8pair_to_f16(d1 >> 8));
+  }
+}
+
+// Quantisation groups below 128 channels (ng = 2 or 4 per token): k-step kk instead holds codes
+// e = 2 kk, 2 kk + 1 of all four units 4*gr + ui, so that each k-step lies in one group
+// (channel u + 16 e is in group e / (8 / ng)).  Slot kg_slot(ui, p) holds unit ui, code e = 2 kk + p.
+template <int KB>
+__host__ __device__ constexpr int kg_slot(int ui, int p) {
+  return KB == 2 ? 2 * ui + p : ui + 4 * p;
+}
+
+template <int KB>
+__device__ __forceinline__ f16x8 dequant_k_grouped(const KRegs<KB>& r, int kk) {
+  if constexpr (KB == 2) {
+    // byte kk / 2 of each 16-bit unit into one dword, its nibble kk % 2 low; then the two 2-bit codes
+    // of each byte into separate nibbles for the fp4 conversion (unit ui in byte ui)
+    const uint32_t b = static_cast<uint32_t>(kk >> 1);
+    const uint32_t sel = b | ((2 + b) << 8) | ((4 + b) << 16) | ((6 + b) << 24);
+    uint32_t x = __builtin_amdgcn_perm(r.w[1], r.w[0], sel);
+    if (kk & 1) x >>= 4;
+    const uint32_t y = (x & 0x03030303u) | ((x << 2) & 0x30303030u);
+    return cat4(fp4b_to_f16<0>(y), fp4b_to_f16<1>(y), fp4b_to_f16<2>(y), fp4b_to_f16<3>(y));
+  } else if constexpr (KB == 4) {
+    // byte kk of the four unit dwords (codes 2 kk low nibble, 2 kk + 1 high nibble) into one dword
+    const uint32_t k = static_cast<uint32_t>(kk);
+    const uint32_t sel = k | ((4 + k) << 8) | 0x0c0c0000u;
+    const uint32_t x = __builtin_amdgcn_perm(r.w[1], r.w[0], sel) | (__builtin_amdgcn_perm(r.w[3], r.w[2], sel) << 16);
+    const uint32_t lo = x & 0x0f0f0f0fu, hi = (x >> 4) & 0x0f0f0f0fu;
+    return cat4(fp8b_to_f16<false>(lo), fp8b_to_f16<true>(lo), fp8b_to_f16<false>(hi), fp8b_to_f16<true>(hi));
+  } else {
+    // bytes 2 kk, 2 kk + 1 of each unit (dword kk / 2 of the unit, half kk % 2): units 0, 1 into d0,
+    // units 2, 3 into d1, as (u even e, u even e+1, u odd e, u odd e+1)
+    const uint32_t h = 2u * static_cast<uint32_t>(kk & 1);
+    const uint32_t sel = h | ((h + 1) << 8) | ((4 + h) << 16) | ((5 + h) << 24);
+    const int dw = kk >> 1;
+    const uint32_t d0 = __builtin_amdgcn_perm(r.w[0][2 + dw], r.w[0][dw], sel);
+    const uint32_t d1 = __builtin_amdgcn_perm(r.w[1][2 + dw], r.w[1][dw], sel);
+    return cat4(u8pair_to_f16(d0), u8pair_to_f16(d1), u8pair_to_f16(d0 >> 8), u8pair_to_f16(d1 >> 8));
   }
 }
 
@@ -250,18 +295,18 @@ __device__ __forceinline__ void load_v_all(VAll<VB, P>& d, const __amdgpu_buffer
     }
 }
 
-// The P pages' six scale arrays (3 KB each, verbatim) into this wave's LDS stage, 1 KB per
-// global_load_lds_dwordx4 (asynchronous, no registers; the compiler waits for it before the first
-// read of that stage).
-template <int KB, int VB, int P>
+// The P pages' scale blocks (2 (1 + 2 NG) KB each, verbatim) into this wave's LDS stage, 1 KB per
+// global_load_lds_dwordx4 (asynchronous, no registers; waited for with vmcnt before the first read).
+template <int KB, int VB, int NG, int P>
 __device__ __forceinline__ void copy_scales(float* stage, const uint8_t* const (&rec)[P], int lane) {
+  constexpr int SC = 2 * half_scale_floats(NG);
   const uint32_t lo = static_cast<uint32_t>(lane * 16);
 #pragma unroll
   for (int e = 0; e < P; ++e) {
     const uint8_t* sbase = rec[e] + scale_offset(KB, VB);
 #pragma unroll
-    for (int c = 0; c < 3; ++c)
-      __builtin_amdgcn_global_load_lds(sbase + (lo + static_cast<uint32_t>(c * 1024)), stage + e * 6 * kCh + c * 256, 16,
+    for (int c = 0; c < SC / 256; ++c)
+      __builtin_amdgcn_global_load_lds(sbase + (lo + static_cast<uint32_t>(c * 1024)), stage + e * SC + c * 256, 16,
                                        0, 0);
   }
 }
@@ -270,25 +315,25 @@ __device__ __forceinline__ f16x8 zero8() {
   return f16x8{0, 0, 0, 0, 0, 0, 0, 0};
 }
 
-}  // namespace
-
 // Pages per wave step P: the 16 MFMA columns are (page, head) pairs.  G = 16 fills them with one
 // page; otherwise a step is two pages (the most whose codes fit the registers of two waves per
 // SIMD), or one for 8-bit K or V codes, and the columns beyond P*G are masked.
-template <int KB, int VB, int G>
+template <int KB, int VB, int G, int NG>
 __host__ __device__ constexpr int decode_pages_per_step() {
-  return G >= 16 ? 1 : ((KB == 8 || VB == 8) ? 1 : 2);
+  return (G >= 16 || NG > 1) ? 1 : ((KB == 8 || VB == 8) ? 1 : 2);
 }
 
-template <int KB, int VB, int G>
+template <int KB, int VB, int G, int NG>
 __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ cache,
                                                         int64_t page_stride, const int32_t* __restrict__ page_table,
                                                         int max_pages, const int32_t* __restrict__ seq_lens,
                                                         int num_q_heads, int num_kv_heads, float qscale,
                                                         float* __restrict__ ws, int n_splits, int groups_per_split) {
-  constexpr int P = decode_pages_per_step<KB, VB, G>();
-  constexpr int R = record_bytes(KB, VB);
-  constexpr int SC = 6 * kCh;   // floats of scales per page
+  constexpr int P = decode_pages_per_step<KB, VB, G, NG>();
+  constexpr int R = record_bytes(KB, VB, NG);
+  constexpr int HS = half_scale_floats(NG);   // floats of one half's scales: c, s'[NG], m'[NG]
+  constexpr int SC = 2 * HS;                   // floats of scales per page
+  static_assert(NG == 1 || P == 1, "grouped formats take one page per step");
   constexpr int MRG = 130;      // floats per merged row
 
   __shared__ float qrot[G][kCh];
@@ -419,34 +464,71 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
       const float4 q4 = *reinterpret_cast<const float4*>(&qrot[g_own][4 * gr + 16 * e8]);
       const float x[4] = {col_ok ? c4.x * q4.x : 0.f, col_ok ? c4.y * q4.y : 0.f, col_ok ? c4.z * q4.z : 0.f,
                           col_ok ? c4.w * q4.w : 0.f};
+      if constexpr (NG == 1) {
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl)
-        if (keperm<KB>(sl) == e8) {
+        for (int sl = 0; sl < 8; ++sl)
+          if (keperm<KB>(sl) == e8) {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const _Float16 hi = static_cast<_Float16>(x[kb]);
-            bqh[kb][sl] = hi;
-            bql[kb][sl] = static_cast<_Float16>(x[kb] - static_cast<float>(hi));
+            for (int kb = 0; kb < 4; ++kb) {
+              const _Float16 hi = static_cast<_Float16>(x[kb]);
+              bqh[kb][sl] = hi;
+              bql[kb][sl] = static_cast<_Float16>(x[kb] - static_cast<float>(hi));
+            }
           }
+      } else {
+        // k-step e8 / 2 holds code e8 of the four units in slots kg_slot(ui, e8 % 2)
+#pragma unroll
+        for (int ui = 0; ui < 4; ++ui) {
+          const _Float16 hi = static_cast<_Float16>(x[ui]);
+          bqh[e8 >> 1][kg_slot<KB>(ui, e8 & 1)] = hi;
+          bql[e8 >> 1][kg_slot<KB>(ui, e8 & 1)] = static_cast<_Float16>(x[ui] - static_cast<float>(hi));
         }
+      }
     }
 
-    // sigma_n = sum_j q''_nj (all rows of the result equal)
-    float sigma;
-    {
+    // sigma_n = sum_j q''_nj over each quantisation group (all rows of the result equal); group g
+    // is k-steps 4g/NG .. 4(g+1)/NG - 1
+    float sigma[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
       f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 4 * g / NG; kb < 4 * (g + 1) / NG; ++kb) {
         d = mfma16(ONES, bqh[kb], d);
         d = mfma16(ONES, bql[kb], d);
       }
-      sigma = d[0];
+      sigma[g] = d[0];
     }
 
     // QK: one accumulator per page; the lane keeps its own page's column
     float lg[8][4];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
+      if constexpr (NG > 1) {
+        // one accumulator per group, each scaled by its own (s', m') of the token
+        f32x4 dg[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) dg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const f16x8 a = dequant_k_grouped<KB>(mb < 4 ? kpre.k[0][mb] : khi.k[0][mb - 4], kb);
+          dg[kb * NG / 4] = mfma16(a, bqh[kb], dg[kb * NG / 4]);
+          dg[kb * NG / 4] = mfma16(a, bql[kb], dg[kb * NG / 4]);
+        }
+        float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const float4 sk = *reinterpret_cast<const float4*>(sown + kCh + kCh * g + 16 * mb + 4 * gr);
+          const float4 mk = *reinterpret_cast<const float4*>(sown + kCh * (1 + NG) + kCh * g + 16 * mb + 4 * gr);
+          l4[0] += fmaf(sk.x, dg[g][0], mk.x * sigma[g]);
+          l4[1] += fmaf(sk.y, dg[g][1], mk.y * sigma[g]);
+          l4[2] += fmaf(sk.z, dg[g][2], mk.z * sigma[g]);
+          l4[3] += fmaf(sk.w, dg[g][3], mk.w * sigma[g]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lg[mb][i] = l4[i];
+        continue;
+      }
       f32x4 d[P];
 #pragma unroll
       for (int e = 0; e < P; ++e) {
@@ -463,10 +545,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
       for (int e = 1; e < P; ++e) dd = (e_own == e) ? d[e] : dd;
       const float4 sk = *reinterpret_cast<const float4*>(sown + 128 + 16 * mb + 4 * gr);
       const float4 mk = *reinterpret_cast<const float4*>(sown + 256 + 16 * mb + 4 * gr);
-      lg[mb][0] = fmaf(sk.x, dd[0], mk.x * sigma);
-      lg[mb][1] = fmaf(sk.y, dd[1], mk.y * sigma);
-      lg[mb][2] = fmaf(sk.z, dd[2], mk.z * sigma);
-      lg[mb][3] = fmaf(sk.w, dd[3], mk.w * sigma);
+      lg[mb][0] = fmaf(sk.x, dd[0], mk.x * sigma[0]);
+      lg[mb][1] = fmaf(sk.y, dd[1], mk.y * sigma[0]);
+      lg[mb][2] = fmaf(sk.z, dd[2], mk.z * sigma[0]);
+      lg[mb][3] = fmaf(sk.w, dd[3], mk.w * sigma[0]);
     }
 
     __builtin_amdgcn_sched_barrier(0);
@@ -487,84 +569,153 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
     const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = m_new;
 
-    // PV weights w_t = p_t s'_t go to the MFMA in fp16.  Their rounding error enters u_j as
-    // sum_t (w~_t - w_t) q_tj; the zero-point term is corrected by -c0 sum_t (w~_t - w_t) with
-    // c0 = (2^b - 1)/2, which centres that error on the codes (q - c0 ~ q + m'/s').
-    constexpr float c0 = 0.5f * ((1 << VB) - 1);
-    f16x8 aw[4];
-    float msum = 0.f, psum = 0.f, wexact = 0.f, wround = 0.f;
+    if constexpr (NG == 1) {
+      // PV weights w_t = p_t s'_t go to the MFMA in fp16.  Their rounding error enters u_j as
+      // sum_t (w~_t - w_t) q_tj; the zero-point term is corrected by -c0 sum_t (w~_t - w_t) with
+      // c0 = (2^b - 1)/2, which centres that error on the codes (q - c0 ~ q + m'/s').
+      constexpr float c0 = 0.5f * ((1 << VB) - 1);
+      f16x8 aw[4];
+      float msum = 0.f, psum = 0.f, wexact = 0.f, wround = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float wv[2][4];
+      for (int kb = 0; kb < 4; ++kb) {
+        float wv[2][4];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int mb = 2 * kb + hh;
-        const float4 sv = *reinterpret_cast<const float4*>(sown + 4 * 128 + 16 * mb + 4 * gr);
-        const float4 mv = *reinterpret_cast<const float4*>(sown + 5 * 128 + 16 * mb + 4 * gr);
-        const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
-        const float mvv[4] = {mv.x, mv.y, mv.z, mv.w};
+        for (int hh = 0; hh < 2; ++hh) {
+          const int mb = 2 * kb + hh;
+          const float4 sv = *reinterpret_cast<const float4*>(sown + 4 * 128 + 16 * mb + 4 * gr);
+          const float4 mv = *reinterpret_cast<const float4*>(sown + 5 * 128 + 16 * mb + 4 * gr);
+          const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
+          const float mvv[4] = {mv.x, mv.y, mv.z, mv.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = (live && valid_own) ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;
-          psum += p;
-          msum = fmaf(p, mvv[i], msum);
-          wv[hh][i] = p * svv[i];
+          for (int i = 0; i < 4; ++i) {
+            const float p = (live && valid_own) ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;
+            psum += p;
+            msum = fmaf(p, mvv[i], msum);
+            wv[hh][i] = p * svv[i];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const _Float16 w0 = static_cast<_Float16>(wv[0][r]);
+          const _Float16 w1 = static_cast<_Float16>(wv[1][r]);
+          aw[kb][vslot<VB>(0, r)] = w0;
+          aw[kb][vslot<VB>(1, r)] = w1;
+          wexact += wv[0][r] + wv[1][r];
+          wround += static_cast<float>(w0) + static_cast<float>(w1);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const _Float16 w0 = static_cast<_Float16>(wv[0][r]);
-        const _Float16 w1 = static_cast<_Float16>(wv[1][r]);
-        aw[kb][vslot<VB>(0, r)] = w0;
-        aw[kb][vslot<VB>(1, r)] = w1;
-        wexact += wv[0][r] + wv[1][r];
-        wround += static_cast<float>(w0) + static_cast<float>(w1);
+      l_part = l_part * alpha + psum;
+      msum = fmaf(-c0, wround - wexact, msum);
+      // sum_t p_t m'_t enters the PV product as one extra k-step (hi/lo fp16 split)
+      f16x8 afake = zero8();
+      {
+        const _Float16 mh = static_cast<_Float16>(msum);
+        const _Float16 ml = static_cast<_Float16>(msum - static_cast<float>(mh));
+        afake[0] = mh;
+        afake[1] = ml;
       }
-    }
-    l_part = l_part * alpha + psum;
-    msum = fmaf(-c0, wround - wexact, msum);
-    // sum_t p_t m'_t enters the PV product as one extra k-step (hi/lo fp16 split)
-    f16x8 afake = zero8();
-    {
-      const _Float16 mh = static_cast<_Float16>(msum);
-      const _Float16 ml = static_cast<_Float16>(msum - static_cast<float>(mh));
-      afake[0] = mh;
-      afake[1] = ml;
-    }
 
-    // alpha of the PV rows 4*gr + i lives in lane 4*gr + i (any row of lanes)
-    float arow[4];
+      // alpha of the PV rows 4*gr + i lives in lane 4*gr + i (any row of lanes)
+      float arow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * gr + i);
-    const float* srow[4];
+      for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * gr + i);
+      const float* srow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) srow[i] = sb + e_rc[i] * SC;
+      for (int i = 0; i < 4; ++i) srow[i] = sb + e_rc[i] * SC;
 
-    // PV: one accumulator per page; the lane keeps its rows' page
+      // PV: one accumulator per page; the lane keeps its rows' page
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      f32x4 d[P];
+      for (int nb = 0; nb < 8; ++nb) {
+        f32x4 d[P];
 #pragma unroll
-      for (int e = 0; e < P; ++e) {
-        d[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < P; ++e) {
+          d[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) d[e] = mfma16(aw[kb], dequant_v<VB>(vc.v[e][nb], kb), d[e]);
+          for (int kb = 0; kb < 4; ++kb) d[e] = mfma16(aw[kb], dequant_v<VB>(vc.v[e][nb], kb), d[e]);
+        }
+        f32x4 dd = d[0];
+#pragma unroll
+        for (int e = 1; e < P; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dd[i] = (e_row[i] == e) ? d[e][i] : dd[i];
+        dd = mfma16(afake, BFAKE, dd);
+        float cv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cv[i] = (G >= 4 || i == 0) ? srow[i][3 * 128 + 16 * nb + nl] : cv[0];
+        if constexpr (G < 4) {
+#pragma unroll
+          for (int i = 1; i < 4; ++i) cv[i] = srow[i][3 * 128 + 16 * nb + nl];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv[i] * dd[i]);
       }
-      f32x4 dd = d[0];
+    } else {
+      // Quantisation groups (one page per step): the softmax numerators once, then per V group gv
+      // (channel blocks nb = EV gv .. EV gv + EV - 1) its weights p_t s'_{t,gv} and zero-point sum.
+      constexpr float c0 = 0.5f * ((1 << VB) - 1);
+      constexpr int EV = 8 / NG;
+      float pr[8][4];
+      float psum = 0.f;
 #pragma unroll
-      for (int e = 1; e < P; ++e)
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dd[i] = (e_row[i] == e) ? d[e][i] : dd[i];
-      dd = mfma16(afake, BFAKE, dd);
-      float cv[4];
+        for (int i = 0; i < 4; ++i) {
+          pr[mb][i] = (live && valid_own) ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;
+          psum += pr[mb][i];
+        }
+      l_part = l_part * alpha + psum;
+      float arow[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cv[i] = (G >= 4 || i == 0) ? srow[i][3 * 128 + 16 * nb + nl] : cv[0];
-      if constexpr (G < 4) {
+      for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * gr + i);
 #pragma unroll
-        for (int i = 1; i < 4; ++i) cv[i] = srow[i][3 * 128 + 16 * nb + nl];
+      for (int gv = 0; gv < NG; ++gv) {
+        f16x8 aw[4];
+        float msum = 0.f, wexact = 0.f, wround = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          float wv[2][4];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int mb = 2 * kb + hh;
+            const float4 sv = *reinterpret_cast<const float4*>(sown + HS + kCh + kCh * gv + 16 * mb + 4 * gr);
+            const float4 mv =
+                *reinterpret_cast<const float4*>(sown + HS + kCh * (1 + NG) + kCh * gv + 16 * mb + 4 * gr);
+            const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
+            const float mvv[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              msum = fmaf(pr[mb][i], mvv[i], msum);
+              wv[hh][i] = pr[mb][i] * svv[i];
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const _Float16 w0 = static_cast<_Float16>(wv[0][r]);
+            const _Float16 w1 = static_cast<_Float16>(wv[1][r]);
+            aw[kb][vslot<VB>(0, r)] = w0;
+            aw[kb][vslot<VB>(1, r)] = w1;
+            wexact += wv[0][r] + wv[1][r];
+            wround += static_cast<float>(w0) + static_cast<float>(w1);
+          }
+        }
+        msum = fmaf(-c0, wround - wexact, msum);
+        f16x8 afake = zero8();
+        {
+          const _Float16 mh = static_cast<_Float16>(msum);
+          afake[0] = mh;
+          afake[1] = static_cast<_Float16>(msum - static_cast<float>(mh));
+        }
+#pragma unroll
+        for (int nb = EV * gv; nb < EV * gv + EV; ++nb) {
+          f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) d = mfma16(aw[kb], dequant_v<VB>(vc.v[0][nb], kb), d);
+          d = mfma16(afake, BFAKE, d);
+          const float cv = sown[HS + 16 * nb + nl];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv * d[i]);
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv[i] * dd[i]);
     }
     // the next group's K codes of blocks 0-3 and its scales, in flight while the next step starts
     __builtin_amdgcn_sched_barrier(0);
@@ -574,7 +725,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
 #pragma unroll
       for (int e = 0; e < P; ++e) rs_n[e] = record_rsrc(rec_next[e], R);
       load_k_half<KB, P>(kpre_next, rs_n, 0, lane);
-      copy_scales<KB, VB, P>(sb_next, rec_next, lane);
+      copy_scales<KB, VB, NG, P>(sb_next, rec_next, lane);
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -592,7 +743,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
 #pragma unroll
       for (int e = 0; e < P; ++e) rs[e] = record_rsrc(ra[e], R);
       load_k_half<KB, P>(ka, rs, 0, lane);
-      copy_scales<KB, VB, P>(sb0, ra, lane);
+      copy_scales<KB, VB, NG, P>(sb0, ra, lane);
     }
     for (int gi = g_begin; gi < g_end; gi += 2) {
       __builtin_amdgcn_sched_barrier(0);
@@ -761,14 +912,62 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict
   o[1] = static_cast<_Float16>((r[1] * kInvSqrt128 + w[1]) * inv_l);
 }
 
-int decode_pages_per_step(int kb, int vb, int group_size) {
-  if (group_size >= 16) return 1;
+template <int KB, int VB, int G, int NG>
+static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64_t page_stride,
+                                  const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                                  const _Float16* tail_k, const _Float16* tail_v, float sm_scale, _Float16* out,
+                                  float* workspace, int num_seqs, int num_q_heads, int num_kv_heads,
+                                  const DecodePlan& plan, hipStream_t stream) {
+  const float qscale = sm_scale * kLog2e * 0.08838834764831845f;
+  hipLaunchKernelGGL((decode_kernel<KB, VB, G, NG>), dim3(num_seqs * num_kv_heads, plan.n_splits), dim3(256), 0, stream,
+                     q, cache, page_stride, page_table, max_pages, seq_lens, num_q_heads, num_kv_heads, qscale,
+                     workspace, plan.n_splits, plan.groups_per_split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(num_seqs * num_q_heads), dim3(256), 0, stream, q, workspace, plan.n_splits,
+                     seq_lens, tail_k, tail_v, num_q_heads, G, sm_scale * kLog2e, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define KVARN_LAUNCHER_NAME2(N) launch_decode_ng##N
+#define KVARN_LAUNCHER_NAME(N) KVARN_LAUNCHER_NAME2(N)
+hipError_t KVARN_LAUNCHER_NAME(KVARN_DECODE_NG)(int kb, int vb, int group_size, const _Float16* q, const uint8_t* cache,
+                                               int64_t page_stride, const int32_t* page_table, int max_pages,
+                                               const int32_t* seq_lens, const _Float16* tail_k, const _Float16* tail_v,
+                                               float sm_scale, _Float16* out, float* workspace, int num_seqs,
+                                               int num_q_heads, int num_kv_heads, const DecodePlan& plan,
+                                               hipStream_t stream) {
+  constexpr int NG = KVARN_DECODE_NG;
+#define KVARN_DECODE_CASE(KB_, VB_, G_)                                                                           \
+  if (kb == KB_ && vb == VB_ && group_size == G_)                                                                 \
+    return launch_decode_t<KB_, VB_, G_, NG>(q, cache, page_stride, page_table, max_pages, seq_lens, tail_k, tail_v, \
+                                             sm_scale, out, workspace, num_seqs, num_q_heads, num_kv_heads, plan,  \
+                                             stream);
+#define KVARN_DECODE_BITS(G_)                                                                               \
+  KVARN_DECODE_CASE(2, 2, G_) KVARN_DECODE_CASE(2, 4, G_) KVARN_DECODE_CASE(2, 8, G_)                       \
+  KVARN_DECODE_CASE(4, 2, G_) KVARN_DECODE_CASE(4, 4, G_) KVARN_DECODE_CASE(4, 8, G_)                       \
+  KVARN_DECODE_CASE(8, 2, G_) KVARN_DECODE_CASE(8, 4, G_) KVARN_DECODE_CASE(8, 8, G_)
+  KVARN_DECODE_BITS(1)
+  KVARN_DECODE_BITS(2)
+  KVARN_DECODE_BITS(4)
+  KVARN_DECODE_BITS(8)
+  KVARN_DECODE_BITS(16)
+#undef KVARN_DECODE_BITS
+#undef KVARN_DECODE_CASE
+  return hipErrorInvalidValue;
+}
+
+#if KVARN_DECODE_NG == 1
+int decode_pages_per_step(int kb, int vb, int ng, int group_size) {
+  if (group_size >= 16 || ng > 1) return 1;
   return (kb == 8 || vb == 8) ? 1 : 2;
 }
 
-DecodePlan plan_decode(int kb, int vb, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq) {
+DecodePlan plan_decode(int kb, int vb, int ng, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq) {
   DecodePlan p;
-  p.pages_per_group = decode_pages_per_step(kb, vb, group_size);
+  p.pages_per_group = decode_pages_per_step(kb, vb, ng, group_size);
   const int groups_max = (max_pages_per_seq + p.pages_per_group - 1) / p.pages_per_group;
   const int units = num_seqs * num_kv_heads;
   const int target_wgs = 512;  // 2 per CU on 256 CUs
@@ -782,84 +981,22 @@ DecodePlan plan_decode(int kb, int vb, int num_seqs, int num_kv_heads, int group
   return p;
 }
 
-bool decode_supported(int kb, int vb, int group_size) {
-  return (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8) &&
+bool decode_supported(int kb, int vb, int ng, int group_size) {
+  return (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8) && (ng == 1 || ng == 2 || ng == 4) &&
          (group_size == 1 || group_size == 2 || group_size == 4 || group_size == 8 || group_size == 16);
 }
 
-template <int KB, int VB, int G>
-static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64_t page_stride,
-                                  const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                                  const _Float16* tail_k, const _Float16* tail_v, float sm_scale, _Float16* out,
-                                  float* workspace, int num_seqs, int num_q_heads, int num_kv_heads,
-                                  const DecodePlan& plan, hipStream_t stream) {
-  const float qscale = sm_scale * kLog2e * 0.08838834764831845f;
-  hipLaunchKernelGGL((decode_kernel<KB, VB, G>), dim3(num_seqs * num_kv_heads, plan.n_splits), dim3(256), 0, stream, q,
-                     cache, page_stride, page_table, max_pages, seq_lens, num_q_heads, num_kv_heads, qscale, workspace,
-                     plan.n_splits, plan.groups_per_split);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(num_seqs * num_q_heads), dim3(256), 0, stream, q, workspace, plan.n_splits,
-                     seq_lens, tail_k, tail_v, num_q_heads, G, sm_scale * kLog2e, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode(int kb, int vb, int group_size, const _Float16* q, const uint8_t* cache, int64_t page_stride,
-                         const int32_t* page_table, int max_pages, const int32_t* seq_lens, const _Float16* tail_k,
-                         const _Float16* tail_v, float sm_scale, _Float16* out, float* workspace, int num_seqs,
-                         int num_q_heads, int num_kv_heads, const DecodePlan& plan, hipStream_t stream) {
+hipError_t launch_decode(int kb, int vb, int ng, int group_size, const _Float16* q, const uint8_t* cache,
+                         int64_t page_stride, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                         const _Float16* tail_k, const _Float16* tail_v, float sm_scale, _Float16* out,
+                         float* workspace, int num_seqs, int num_q_heads, int num_kv_heads, const DecodePlan& plan,
+                         hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
-#define KVARN_DECODE_CASE(KB_, VB_, G_)                                                                          \
-  if (kb == KB_ && vb == VB_ && group_size == G_)                                                                \
-    return launch_decode_t<KB_, VB_, G_>(q, cache, page_stride, page_table, max_pages, seq_lens, tail_k, tail_v, \
-                                         sm_scale, out, workspace, num_seqs, num_q_heads, num_kv_heads, plan, stream);
-  KVARN_DECODE_CASE(2, 2, 1)
-  KVARN_DECODE_CASE(2, 4, 1)
-  KVARN_DECODE_CASE(2, 8, 1)
-  KVARN_DECODE_CASE(4, 2, 1)
-  KVARN_DECODE_CASE(4, 4, 1)
-  KVARN_DECODE_CASE(4, 8, 1)
-  KVARN_DECODE_CASE(8, 2, 1)
-  KVARN_DECODE_CASE(8, 4, 1)
-  KVARN_DECODE_CASE(8, 8, 1)
-  KVARN_DECODE_CASE(2, 2, 2)
-  KVARN_DECODE_CASE(2, 4, 2)
-  KVARN_DECODE_CASE(2, 8, 2)
-  KVARN_DECODE_CASE(4, 2, 2)
-  KVARN_DECODE_CASE(4, 4, 2)
-  KVARN_DECODE_CASE(4, 8, 2)
-  KVARN_DECODE_CASE(8, 2, 2)
-  KVARN_DECODE_CASE(8, 4, 2)
-  KVARN_DECODE_CASE(8, 8, 2)
-  KVARN_DECODE_CASE(2, 2, 4)
-  KVARN_DECODE_CASE(2, 4, 4)
-  KVARN_DECODE_CASE(2, 8, 4)
-  KVARN_DECODE_CASE(4, 2, 4)
-  KVARN_DECODE_CASE(4, 4, 4)
-  KVARN_DECODE_CASE(4, 8, 4)
-  KVARN_DECODE_CASE(8, 2, 4)
-  KVARN_DECODE_CASE(8, 4, 4)
-  KVARN_DECODE_CASE(8, 8, 4)
-  KVARN_DECODE_CASE(2, 2, 8)
-  KVARN_DECODE_CASE(2, 4, 8)
-  KVARN_DECODE_CASE(2, 8, 8)
-  KVARN_DECODE_CASE(4, 2, 8)
-  KVARN_DECODE_CASE(4, 4, 8)
-  KVARN_DECODE_CASE(4, 8, 8)
-  KVARN_DECODE_CASE(8, 2, 8)
-  KVARN_DECODE_CASE(8, 4, 8)
-  KVARN_DECODE_CASE(8, 8, 8)
-  KVARN_DECODE_CASE(2, 2, 16)
-  KVARN_DECODE_CASE(2, 4, 16)
-  KVARN_DECODE_CASE(2, 8, 16)
-  KVARN_DECODE_CASE(4, 2, 16)
-  KVARN_DECODE_CASE(4, 4, 16)
-  KVARN_DECODE_CASE(4, 8, 16)
-  KVARN_DECODE_CASE(8, 2, 16)
-  KVARN_DECODE_CASE(8, 4, 16)
-  KVARN_DECODE_CASE(8, 8, 16)
-#undef KVARN_DECODE_CASE
-  return hipErrorInvalidValue;
+  auto* fn = ng == 1 ? launch_decode_ng1 : ng == 2 ? launch_decode_ng2 : ng == 4 ? launch_decode_ng4 : nullptr;
+  if (fn == nullptr) return hipErrorInvalidValue;
+  return fn(kb, vb, group_size, q, cache, page_stride, page_table, max_pages, seq_lens, tail_k, tail_v, sm_scale, out,
+            workspace, num_seqs, num_q_heads, num_kv_heads, plan, stream);
 }
+#endif
 
 }  // namespace kvarn

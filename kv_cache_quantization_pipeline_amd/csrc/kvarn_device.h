@@ -25,7 +25,11 @@ constexpr int kCh = 128;     // head_dim
 __host__ __device__ constexpr int k_code_bytes(int kb) { return kTok * kCh * kb / 8; }
 __host__ __device__ constexpr int v_code_bytes(int vb) { return kTok * kCh * vb / 8; }
 __host__ __device__ constexpr int scale_offset(int kb, int vb) { return k_code_bytes(kb) + v_code_bytes(vb); }
-__host__ __device__ constexpr int record_bytes(int kb, int vb) { return scale_offset(kb, vb) + 6 * kCh * 4; }
+// One half's scale block (floats): c[128], s'[ng][128], m'[ng][128]; ng = 128 / group.
+__host__ __device__ constexpr int half_scale_floats(int ng) { return kCh * (1 + 2 * ng); }
+__host__ __device__ constexpr int record_bytes(int kb, int vb, int ng) {
+  return scale_offset(kb, vb) + 2 * half_scale_floats(ng) * 4;
+}
 
 // ---- lane primitives --------------------------------------------------------
 __device__ __forceinline__ float as_f(uint32_t x) { return __builtin_bit_cast(float, x); }

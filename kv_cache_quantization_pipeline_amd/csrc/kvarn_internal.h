@@ -6,13 +6,14 @@
 
 namespace kvarn {
 
+// ng: quantisation groups per token (128 / group size): 1, 2 or 4.
 hipError_t launch_quantize_tiles(const _Float16* k, const _Float16* v, const int32_t* dst_pages, uint8_t* cache,
-                                 int64_t page_stride, int num_tiles, int num_kv_heads, int kb, int vb, int iters,
-                                 hipStream_t stream);
+                                 int64_t page_stride, int num_tiles, int num_kv_heads, int kb, int vb, int ng,
+                                 int iters, hipStream_t stream);
 
 hipError_t launch_append(const _Float16* k_new, const _Float16* v_new, int32_t* seq_lens, _Float16* tail_k,
                          _Float16* tail_v, const int32_t* page_table, int max_pages, uint8_t* cache,
-                         int64_t page_stride, int num_seqs, int num_kv_heads, int kb, int vb, int iters,
+                         int64_t page_stride, int num_seqs, int num_kv_heads, int kb, int vb, int ng, int iters,
                          hipStream_t stream);
 
 // Split-K decode plan: the grid is (num_seqs*num_kv_heads, n_splits) workgroups of 4 waves;
@@ -22,18 +23,31 @@ struct DecodePlan {
   int groups_per_split;
   int n_splits;
 };
-int decode_pages_per_step(int kb, int vb, int group_size);
-DecodePlan plan_decode(int kb, int vb, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq);
+// ng: quantisation groups per token (1, 2, 4); group_size: query heads per kv head.
+int decode_pages_per_step(int kb, int vb, int ng, int group_size);
+DecodePlan plan_decode(int kb, int vb, int ng, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq);
 
 // Workspace floats per (sequence, query head, split): running max, running sum, two pad floats
 // (16-byte alignment of what follows), 128 accumulators.
 constexpr int kPartialFloats = 132;
 
-bool decode_supported(int kb, int vb, int group_size);
+bool decode_supported(int kb, int vb, int ng, int group_size);
 
-hipError_t launch_decode(int kb, int vb, int group_size, const _Float16* q, const uint8_t* cache, int64_t page_stride,
+hipError_t launch_decode(int kb, int vb, int ng, int group_size, const _Float16* q, const uint8_t* cache, int64_t page_stride,
                          const int32_t* page_table, int max_pages, const int32_t* seq_lens, const _Float16* tail_k,
                          const _Float16* tail_v, float sm_scale, _Float16* out, float* workspace, int num_seqs,
                          int num_q_heads, int num_kv_heads, const DecodePlan& plan, hipStream_t stream);
+// The kernels of one group count (ng = 1, 2, 4), each in its own object.
+#define KVARN_DECL_LAUNCHER(N)                                                                                       \
+  hipError_t launch_decode_ng##N(int kb, int vb, int group_size, const _Float16* q, const uint8_t* cache,            \
+                                 int64_t page_stride, const int32_t* page_table, int max_pages,                      \
+                                 const int32_t* seq_lens, const _Float16* tail_k, const _Float16* tail_v,            \
+                                 float sm_scale, _Float16* out, float* workspace, int num_seqs, int num_q_heads,     \
+                                 int num_kv_heads, const DecodePlan& plan, hipStream_t stream);
+KVARN_DECL_LAUNCHER(1)
+KVARN_DECL_LAUNCHER(2)
+KVARN_DECL_LAUNCHER(4)
+#undef KVARN_DECL_LAUNCHER
+
 
 }  // namespace kvarn

@@ -15,7 +15,8 @@ bool bits_ok(int b) { return b == 2 || b == 4 || b == 8; }
 kvarn_status check_format(const kvarn_format* f) {
   if (f == nullptr) return KVARN_E_INVALID_ARG;
   if (!bits_ok(f->k_bits) || !bits_ok(f->v_bits)) return KVARN_E_UNSUPPORTED;
-  if (f->group != 128 || f->head_dim != 128 || f->block_size != 128) return KVARN_E_UNSUPPORTED;
+  if (f->head_dim != 128 || f->block_size != 128) return KVARN_E_UNSUPPORTED;
+  if (f->group != 128 && f->group != 64 && f->group != 32) return KVARN_E_UNSUPPORTED;
   if (f->sinkhorn_iters < 0 || f->sinkhorn_iters > 64) return KVARN_E_INVALID_ARG;
   return KVARN_OK;
 }
@@ -34,6 +35,11 @@ bool parse_int(const char*& p, int* out) {
 }
 
 kvarn_status hip_status(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_E_HIP; }
+
+// quantisation groups per token
+int n_groups(const kvarn_format* f) { return 128 / f->group; }
+
+int64_t record_bytes(const kvarn_format* f) { return kvarn::record_bytes(f->k_bits, f->v_bits, n_groups(f)); }
 
 }  // namespace
 
@@ -63,7 +69,7 @@ kvarn_status kvarn_format_check(const kvarn_format* f) { return check_format(f);
 
 size_t kvarn_record_bytes(const kvarn_format* f) {
   if (check_format(f) != KVARN_OK) return 0;
-  return static_cast<size_t>(kvarn::record_bytes(f->k_bits, f->v_bits));
+  return static_cast<size_t>(record_bytes(f));
 }
 
 size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
@@ -72,8 +78,9 @@ size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int
       num_q_heads % num_kv_heads != 0 || max_pages_per_seq < 0)
     return 0;
   const int G = num_q_heads / num_kv_heads;
-  if (!kvarn::decode_supported(f->k_bits, f->v_bits, G)) return 0;
-  const kvarn::DecodePlan plan = kvarn::plan_decode(f->k_bits, f->v_bits, num_seqs, num_kv_heads, G, max_pages_per_seq);
+  if (!kvarn::decode_supported(f->k_bits, f->v_bits, n_groups(f), G)) return 0;
+  const kvarn::DecodePlan plan =
+      kvarn::plan_decode(f->k_bits, f->v_bits, n_groups(f), num_seqs, num_kv_heads, G, max_pages_per_seq);
   return static_cast<size_t>(num_seqs) * num_q_heads * plan.n_splits * kvarn::kPartialFloats * sizeof(float);
 }
 
@@ -85,12 +92,13 @@ kvarn_status kvarn_quantize_tiles(const kvarn_format* f, int32_t num_tiles, int3
   if (num_tiles < 0 || num_kv_heads <= 0) return KVARN_E_INVALID_ARG;
   if (num_tiles == 0) return KVARN_OK;
   if (k == nullptr || v == nullptr || dst_pages == nullptr || cache == nullptr) return KVARN_E_INVALID_ARG;
-  const int64_t R = kvarn::record_bytes(f->k_bits, f->v_bits);
+  const int64_t R = record_bytes(f);
   if (page_stride_bytes < R * num_kv_heads || page_stride_bytes % 16 != 0) return KVARN_E_INVALID_ARG;
   if (static_cast<int64_t>(num_tiles) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
   return hip_status(kvarn::launch_quantize_tiles(static_cast<const _Float16*>(k), static_cast<const _Float16*>(v),
                                                  dst_pages, static_cast<uint8_t*>(cache), page_stride_bytes, num_tiles,
-                                                 num_kv_heads, f->k_bits, f->v_bits, f->sinkhorn_iters, stream));
+                                                 num_kv_heads, f->k_bits, f->v_bits, n_groups(f), f->sinkhorn_iters,
+                                                 stream));
 }
 
 kvarn_status kvarn_append_token(const kvarn_format* f, int32_t num_seqs, int32_t num_kv_heads, const void* k_new,
@@ -104,13 +112,13 @@ kvarn_status kvarn_append_token(const kvarn_format* f, int32_t num_seqs, int32_t
   if (k_new == nullptr || v_new == nullptr || seq_lens == nullptr || tail_k == nullptr || tail_v == nullptr ||
       page_table == nullptr || cache == nullptr)
     return KVARN_E_INVALID_ARG;
-  const int64_t R = kvarn::record_bytes(f->k_bits, f->v_bits);
+  const int64_t R = record_bytes(f);
   if (page_stride_bytes < R * num_kv_heads || page_stride_bytes % 16 != 0) return KVARN_E_INVALID_ARG;
   if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
   return hip_status(kvarn::launch_append(
       static_cast<const _Float16*>(k_new), static_cast<const _Float16*>(v_new), seq_lens,
       static_cast<_Float16*>(tail_k), static_cast<_Float16*>(tail_v), page_table, max_pages_per_seq,
-      static_cast<uint8_t*>(cache), page_stride_bytes, num_seqs, num_kv_heads, f->k_bits, f->v_bits,
+      static_cast<uint8_t*>(cache), page_stride_bytes, num_seqs, num_kv_heads, f->k_bits, f->v_bits, n_groups(f),
       f->sinkhorn_iters, stream));
 }
 
@@ -124,20 +132,21 @@ kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int
   if (num_seqs < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_pages_per_seq < 0) return KVARN_E_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return KVARN_E_INVALID_ARG;
   const int G = num_q_heads / num_kv_heads;
-  if (!kvarn::decode_supported(f->k_bits, f->v_bits, G)) return KVARN_E_UNSUPPORTED;
+  if (!kvarn::decode_supported(f->k_bits, f->v_bits, n_groups(f), G)) return KVARN_E_UNSUPPORTED;
   if (num_seqs == 0) return KVARN_OK;
   if (q == nullptr || cache == nullptr || page_table == nullptr || seq_lens == nullptr || tail_k == nullptr ||
       tail_v == nullptr || out == nullptr || workspace == nullptr)
     return KVARN_E_INVALID_ARG;
-  const int64_t R = kvarn::record_bytes(f->k_bits, f->v_bits);
+  const int64_t R = record_bytes(f);
   if (page_stride_bytes < R * num_kv_heads || page_stride_bytes % 16 != 0) return KVARN_E_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return KVARN_E_INVALID_ARG;
   if (workspace_bytes < kvarn_decode_workspace_bytes(f, num_seqs, num_q_heads, num_kv_heads, max_pages_per_seq))
     return KVARN_E_INVALID_ARG;
   if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
-  const kvarn::DecodePlan plan = kvarn::plan_decode(f->k_bits, f->v_bits, num_seqs, num_kv_heads, G, max_pages_per_seq);
+  const kvarn::DecodePlan plan =
+      kvarn::plan_decode(f->k_bits, f->v_bits, n_groups(f), num_seqs, num_kv_heads, G, max_pages_per_seq);
   if (plan.n_splits > 65535) return KVARN_E_UNSUPPORTED;
-  return hip_status(kvarn::launch_decode(f->k_bits, f->v_bits, G, static_cast<const _Float16*>(q),
+  return hip_status(kvarn::launch_decode(f->k_bits, f->v_bits, n_groups(f), G, static_cast<const _Float16*>(q),
                                          static_cast<const uint8_t*>(cache), page_stride_bytes, page_table,
                                          max_pages_per_seq, seq_lens, static_cast<const _Float16*>(tail_k),
                                          static_cast<const _Float16*>(tail_v), sm_scale, static_cast<_Float16*>(out),

@@ -13,7 +13,7 @@
 //      is one FMA per element plus lane reductions (DPP row rotations for the
 //      16 lanes that share a token, permlane16/32 swaps for the 4 lane rows
 //      that share a channel, LDS for the partner wave),
-//   4. asymmetric RTN per token group of 128 channels and sub-byte packing
+//   4. asymmetric RTN per token group (128, 64 or 32 contiguous channels) and sub-byte packing
 //      straight from the MFMA result layout into the record layout.
 // Scaling: with Ytilde = sqrt(128) Y the channel log-scales come out shifted by
 // ln(128)/2 and the token log-scales unchanged; the stored values are
@@ -80,10 +80,10 @@ __device__ __forceinline__ void pack_codes(F f, uint32_t (&w)[NW]) {
   }
 }
 
-// Codes and stores for one tile half once the channel sums S~_j are known.  R holds Ytilde on
-// entry and W = Ytilde exp(-v~) (= Y exp(-v)) afterwards.
+// Codes and stores for one tile half once the channel sums S~_j are known, one quantisation group
+// per token (g128).  R holds Ytilde on entry and W = Ytilde exp(-v~) (= Y exp(-v)) afterwards.
 template <int BITS>
-__device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[8], uint8_t* rec, int code_off,
+__device__ __forceinline__ void quantize_store_g128(TileRegs& R, const float (&sfin)[8], uint8_t* rec, int code_off,
                                                int scale_off, bool is_v, int half, int gr, int nl, WaveLds& L) {
   constexpr int qmax = (1 << BITS) - 1;
 #pragma unroll
@@ -203,6 +203,164 @@ __device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[
   }
 }
 
+// Pack codes c = c0 .. c1-1 of N (unrounded value f(c)) at bit BITS*c of the words w, OR-ed into
+// what w holds: code c goes to byte (BITS*c % 32) / 8 of sub-word (BITS*c % 8) / BITS through
+// v_cvt_pk_u8_f32 (round to nearest, ties to even, clamp to [0, 255], insert as one byte), and the
+// 8/BITS sub-words of a word are merged with shifts by BITS.  c0 and c1 are constants once the
+// caller's loops are unrolled.
+template <int BITS, int N, class F, int NW>
+__device__ __forceinline__ void pack_codes_or(F f, int c0, int c1, uint32_t (&w)[NW]) {
+  constexpr int NS = 8 / BITS;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    if ((BITS * c0) / 32 > k || (BITS * (c1 - 1)) / 32 < k) continue;
+    uint32_t d[NS];
+#pragma unroll
+    for (int sw = 0; sw < NS; ++sw) d[sw] = 0;
+#pragma unroll
+    for (int c = 0; c < N; ++c)
+      if (c >= c0 && c < c1 && (BITS * c) / 32 == k)
+        d[(BITS * c % 8) / BITS] = __builtin_amdgcn_cvt_pk_u8_f32(f(c), (BITS * c % 32) / 8, d[(BITS * c % 8) / BITS]);
+    uint32_t u = d[0];
+#pragma unroll
+    for (int sw = 1; sw < NS; ++sw) u |= d[sw] << (BITS * sw);
+    w[k] |= u;
+  }
+}
+
+// Codes and stores for one tile half once the channel sums S~_j are known, NG > 1 quantisation
+// groups per token.  R holds Ytilde on entry and W = Ytilde exp(-v~) (= Y exp(-v)) afterwards.
+// Each token's channels form NG groups of 128/NG contiguous channels (channel blocks nb = EG*gi .. EG*gi + EG - 1 of group gi), each with
+// its own (mn, s); the groups are done one after the other so that only one group's per-token
+// (mn, 1/s) is held in registers.
+template <int BITS, int NG>
+__device__ __forceinline__ void quantize_store(TileRegs& R, const float (&sfin)[8], uint8_t* rec, int code_off,
+                                               int scale_off, bool is_v, int half, int gr, int nl, WaveLds& L) {
+  constexpr int qmax = (1 << BITS) - 1;
+  constexpr int EG = 8 / NG;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const float b = __builtin_amdgcn_rsqf(sfin[nb]);  // exp(-v~_j)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) R.y[mb][nb] *= b;
+  }
+
+  float* sc = reinterpret_cast<float*>(rec + scale_off);
+  const int lane = 16 * gr + nl;
+  // the token whose statistics this lane reduces: k = nl = 4*mb + i of its lane row
+  const int t_own = 64 * half + 16 * (nl >> 2) + 4 * gr + (nl & 3);
+  if (half == 0 && gr == 0) {
+    // c_j = sqrt(S~_j / 128) = S~_j rsq(S~_j) / sqrt(128), within 2 ulp; exactly 1 for S~_j = 128
+    // (an all-zero channel)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const float c = sfin[nb] * __builtin_amdgcn_rsqf(sfin[nb]) * 0.08838834764831845f;
+      sc[16 * nb + nl] = sfin[nb] == 128.0f ? 1.0f : c;
+    }
+  }
+
+  // K units of this lane's 16 tokens (channels nl + 16e, e = nb), filled group by group
+  constexpr int KW = BITS == 8 ? 2 : 1;
+  uint32_t kw[4][4][KW];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < KW; ++k) kw[mb][i][k] = 0;
+
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    // per-(token, group) min / max: this lane's EG channels, then the 16 lanes of the row through
+    // an LDS transpose (lane nl of a row reduces token k = nl = 4*mb + i of that row)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mn = R.y[mb][EG * gi][i], mx = mn;
+#pragma unroll
+        for (int nb = EG * gi + 1; nb < EG * gi + EG; ++nb) {
+          mn = fminf(mn, R.y[mb][nb][i]);
+          mx = fmaxf(mx, R.y[mb][nb][i]);
+        }
+        *reinterpret_cast<float2*>(&L.tb[lane][2 * (4 * mb + i)]) = make_float2(mn, mx);
+      }
+    __builtin_amdgcn_wave_barrier();
+    float mn_own, mx_own;
+    {
+      const float2 v0 = *reinterpret_cast<const float2*>(&L.tb[16 * gr][2 * nl]);
+      mn_own = v0.x;
+      mx_own = v0.y;
+#pragma unroll
+      for (int l = 1; l < 16; ++l) {
+        const float2 v = *reinterpret_cast<const float2*>(&L.tb[16 * gr + l][2 * nl]);
+        mn_own = fminf(mn_own, v.x);
+        mx_own = fmaxf(mx_own, v.y);
+      }
+    }
+    {
+      const float range = mx_own - mn_own;
+      const float inv_own = range > 0.f ? qmax * fast_rcp(range) : 0.f;
+      sc[kCh + kCh * gi + t_own] = range * (1.0f / qmax);
+      sc[kCh + kCh * NG + kCh * gi + t_own] = mn_own;
+      *reinterpret_cast<float2*>(&L.wb[gr][2 * nl]) = make_float2(mn_own, inv_own);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float inv[4][4], nmi[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const float4 v = *reinterpret_cast<const float4*>(&L.wb[gr][8 * mb + 4 * ii]);
+        inv[mb][2 * ii] = v.y;
+        nmi[mb][2 * ii] = -v.x * v.y;
+        inv[mb][2 * ii + 1] = v.w;
+        nmi[mb][2 * ii + 1] = -v.z * v.w;
+      }
+    __builtin_amdgcn_wave_barrier();
+
+    // (W - mn) * inv as one FMA; v_cvt_pk_u8_f32 rounds it to the nearest integer (ties to even),
+    // clamps to [0, 255] and inserts it as one byte of a word
+    auto val = [&](int mb, int nb, int i) -> float { return fmaf(R.y[mb][nb][i], inv[mb][i], nmi[mb][i]); };
+    if (!is_v) {
+      // K unit of token t, lane nl: channels nl + 16e at bit BITS*e; stored with its last group
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pack_codes_or<BITS, 8>([&](int e) { return val(mb, e, i); }, EG * gi, EG * gi + EG, kw[mb][i]);
+          if (gi == NG - 1) {
+            const int t = 64 * half + 16 * mb + 4 * gr + i;
+            uint8_t* p = rec + code_off + t * 16 * BITS + nl * BITS;
+            if constexpr (BITS == 8)
+              *reinterpret_cast<u32x2*>(p) = u32x2{kw[mb][i][0], kw[mb][i][1]};
+            else if constexpr (BITS == 4)
+              *reinterpret_cast<uint32_t*>(p) = kw[mb][i][0];
+            else
+              *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(kw[mb][i][0]);
+          }
+        }
+    } else {
+      // V unit (nb, gr, nl, half): tokens (mb, i) at bit BITS*(4mb + i)
+#pragma unroll
+      for (int nb = EG * gi; nb < EG * gi + EG; ++nb) {
+        uint8_t* p = rec + code_off + ((nb * 4 + gr) * 16 + nl) * 4 * BITS + half * 2 * BITS;
+        constexpr int W = BITS / 2;  // 32-bit words per unit
+        uint32_t u[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) u[k] = 0;
+        pack_codes_or<BITS, 16>([&](int c) { return val(c >> 2, nb, c & 3); }, 0, 16, u);
+        if constexpr (W == 1)
+          *reinterpret_cast<uint32_t*>(p) = u[0];
+        else if constexpr (W == 2)
+          *reinterpret_cast<u32x2*>(p) = u32x2{u[0], u[1]};
+        else
+          *reinterpret_cast<u32x4*>(p) = u32x4{u[0], u[1], u[2], u[3]};
+      }
+    }
+  }
+}
+
 // MFMA A operands of this wave's 64 tokens: token 16*mb + nl, channels 32*k4 + 8*gr + s.
 __device__ __forceinline__ void load_x(f16x8 (&xa)[4][4], const _Float16* __restrict__ x, int64_t row_stride,
                                        const _Float16* __restrict__ last_row, int half, int gr, int nl) {
@@ -248,7 +406,7 @@ __device__ __forceinline__ void rotate(const f16x8 (&xa)[4][4], TileRegs& R, int
 // Quantise the tile half owned by this pair of waves and write its part of the
 // record.  x: token 0, channel 0; row t at x + t*row_stride (halves); when
 // last_row is non-null token 127 is read from there.  xch: LDS [2][4][64].
-template <int KB, int VB>
+template <int KB, int VB, int NG>
 __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ x, int64_t row_stride,
                                                    const _Float16* __restrict__ last_row, uint8_t* __restrict__ rec,
                                                    int iters, float2 (*xch)[4][64], WaveLds* wlds) {
@@ -377,14 +535,21 @@ __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ 
   }
   // 4. codes, scales, stores
   const int code_off = is_v ? k_code_bytes(KB) : 0;
-  const int scale_off = scale_offset(KB, VB) + (is_v ? 3 * 512 : 0);
-  if (is_v)
-    quantize_store<VB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl, L);
-  else
-    quantize_store<KB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl, L);
+  const int scale_off = scale_offset(KB, VB) + (is_v ? half_scale_floats(NG) * 4 : 0);
+  if constexpr (NG == 1) {
+    if (is_v)
+      quantize_store_g128<VB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl, L);
+    else
+      quantize_store_g128<KB>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl, L);
+  } else {
+    if (is_v)
+      quantize_store<VB, NG>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl, L);
+    else
+      quantize_store<KB, NG>(R, sfin, rec, code_off, scale_off, is_v, half, gr, nl, L);
+  }
 }
 
-template <int KB, int VB>
+template <int KB, int VB, int NG>
 __global__ __launch_bounds__(256, 2) void quantize_tiles_kernel(const _Float16* __restrict__ k,
                                                                 const _Float16* __restrict__ v,
                                                                 const int32_t* __restrict__ dst_pages,
@@ -398,14 +563,14 @@ __global__ __launch_bounds__(256, 2) void quantize_tiles_kernel(const _Float16* 
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * kCh;
   const _Float16* src = (is_v ? v : k) + (static_cast<int64_t>(tile) * kTok * num_kv_heads + h) * kCh;
   uint8_t* rec = cache + static_cast<int64_t>(dst_pages[tile]) * page_stride +
-                 static_cast<int64_t>(h) * record_bytes(KB, VB);
-  quantize_tile_half<KB, VB>(src, row_stride, nullptr, rec, iters, xch, wlds);
+                 static_cast<int64_t>(h) * record_bytes(KB, VB, NG);
+  quantize_tile_half<KB, VB, NG>(src, row_stride, nullptr, rec, iters, xch, wlds);
 }
 
 // Token append: one workgroup per (sequence, kv head).  Writes the new token into
 // the fp16 tail at len % 128 and, when that fills the tile, quantises the tail
 // (token 127 read from the new token itself) into page_table[s][len / 128].
-template <int KB, int VB>
+template <int KB, int VB, int NG>
 __global__ __launch_bounds__(256, 2) void append_kernel(const _Float16* __restrict__ k_new,
                                                         const _Float16* __restrict__ v_new,
                                                         const int32_t* __restrict__ seq_lens,
@@ -433,8 +598,9 @@ __global__ __launch_bounds__(256, 2) void append_kernel(const _Float16* __restri
     const _Float16* x = (is_v ? tail_v : tail_k) + tail_base;
     const _Float16* last = (is_v ? v_new : k_new) + static_cast<int64_t>(sh) * kCh;
     const int page = page_table[static_cast<int64_t>(s) * max_pages + (len >> 7)];
-    uint8_t* rec = cache + static_cast<int64_t>(page) * page_stride + static_cast<int64_t>(h) * record_bytes(KB, VB);
-    quantize_tile_half<KB, VB>(x, kCh, last, rec, iters, xch, wlds);
+    uint8_t* rec =
+        cache + static_cast<int64_t>(page) * page_stride + static_cast<int64_t>(h) * record_bytes(KB, VB, NG);
+    quantize_tile_half<KB, VB, NG>(x, kCh, last, rec, iters, xch, wlds);
   }
 }
 
@@ -443,18 +609,20 @@ __global__ void seq_len_increment_kernel(int32_t* __restrict__ seq_lens, int n) 
   if (i < n) seq_lens[i] += 1;
 }
 
-// (kb, vb) -> the kernel instantiation for that format
-#define KVARN_FOR_EACH_FORMAT(X) X(2, 2) X(2, 4) X(2, 8) X(4, 2) X(4, 4) X(4, 8) X(8, 2) X(8, 4) X(8, 8)
+// (kb, vb, groups per token) -> the kernel instantiation for that format
+#define KVARN_FOR_EACH_BITS(X, NG) \
+  X(2, 2, NG) X(2, 4, NG) X(2, 8, NG) X(4, 2, NG) X(4, 4, NG) X(4, 8, NG) X(8, 2, NG) X(8, 4, NG) X(8, 8, NG)
+#define KVARN_FOR_EACH_FORMAT(X) KVARN_FOR_EACH_BITS(X, 1) KVARN_FOR_EACH_BITS(X, 2) KVARN_FOR_EACH_BITS(X, 4)
 
 hipError_t launch_quantize_tiles(const _Float16* k, const _Float16* v, const int32_t* dst_pages, uint8_t* cache,
-                                 int64_t page_stride, int num_tiles, int num_kv_heads, int kb, int vb, int iters,
-                                 hipStream_t stream) {
+                                 int64_t page_stride, int num_tiles, int num_kv_heads, int kb, int vb, int ng,
+                                 int iters, hipStream_t stream) {
   if (num_tiles == 0) return hipSuccess;
-#define KVARN_Q(KB_, VB_)                                                                                          \
-  if (kb == KB_ && vb == VB_) {                                                                                    \
-    hipLaunchKernelGGL((quantize_tiles_kernel<KB_, VB_>), dim3(num_tiles * num_kv_heads), dim3(256), 0, stream, k, \
-                       v, dst_pages, cache, page_stride, num_kv_heads, iters);                                     \
-    return hipGetLastError();                                                                                      \
+#define KVARN_Q(KB_, VB_, NG_)                                                                                      \
+  if (kb == KB_ && vb == VB_ && ng == NG_) {                                                                        \
+    hipLaunchKernelGGL((quantize_tiles_kernel<KB_, VB_, NG_>), dim3(num_tiles * num_kv_heads), dim3(256), 0, stream, \
+                       k, v, dst_pages, cache, page_stride, num_kv_heads, iters);                                   \
+    return hipGetLastError();                                                                                       \
   }
   KVARN_FOR_EACH_FORMAT(KVARN_Q)
 #undef KVARN_Q
@@ -463,16 +631,16 @@ hipError_t launch_quantize_tiles(const _Float16* k, const _Float16* v, const int
 
 hipError_t launch_append(const _Float16* k_new, const _Float16* v_new, int32_t* seq_lens, _Float16* tail_k,
                          _Float16* tail_v, const int32_t* page_table, int max_pages, uint8_t* cache,
-                         int64_t page_stride, int num_seqs, int num_kv_heads, int kb, int vb, int iters,
+                         int64_t page_stride, int num_seqs, int num_kv_heads, int kb, int vb, int ng, int iters,
                          hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
   hipError_t e = hipErrorInvalidValue;
-#define KVARN_A(KB_, VB_)                                                                                       \
-  if (kb == KB_ && vb == VB_) {                                                                                 \
-    hipLaunchKernelGGL((append_kernel<KB_, VB_>), dim3(num_seqs * num_kv_heads), dim3(256), 0, stream, k_new,   \
-                       v_new, seq_lens, tail_k, tail_v, page_table, max_pages, cache, page_stride, num_kv_heads, \
-                       iters);                                                                                  \
-    e = hipGetLastError();                                                                                      \
+#define KVARN_A(KB_, VB_, NG_)                                                                                     \
+  if (kb == KB_ && vb == VB_ && ng == NG_) {                                                                       \
+    hipLaunchKernelGGL((append_kernel<KB_, VB_, NG_>), dim3(num_seqs * num_kv_heads), dim3(256), 0, stream, k_new, \
+                       v_new, seq_lens, tail_k, tail_v, page_table, max_pages, cache, page_stride, num_kv_heads,    \
+                       iters);                                                                                     \
+    e = hipGetLastError();                                                                                         \
   }
   KVARN_FOR_EACH_FORMAT(KVARN_A)
 #undef KVARN_A

@@ -30,6 +30,8 @@ def test_library_exports_every_header_symbol():
     ("kvarn_k4v2_g128", (4, 2, 128, 128, 128, 8)),
     ("kvarn_k8v8_g128", (8, 8, 128, 128, 128, 8)),
     ("kvarn_k2v4_g128", (2, 4, 128, 128, 128, 8)),
+    ("kvarn_k4v2_g64", (4, 2, 64, 128, 128, 8)),
+    ("kvarn_k8v4_g32", (8, 4, 32, 128, 128, 8)),
 ])
 def test_format_parse(name, expect):
     f = kv.format_parse(name)
@@ -37,7 +39,8 @@ def test_format_parse(name, expect):
 
 
 @pytest.mark.parametrize("name,status", [
-    ("kvarn_k4v2_g64", kv.KVARN_E_UNSUPPORTED),
+    ("kvarn_k4v2_g16", kv.KVARN_E_UNSUPPORTED),
+    ("kvarn_k4v2_g256", kv.KVARN_E_UNSUPPORTED),
     ("kvarn_k3v2_g128", kv.KVARN_E_UNSUPPORTED),
     ("kvarn_k4v16_g128", kv.KVARN_E_UNSUPPORTED),
     ("kvarn_k4v2", kv.KVARN_E_INVALID_ARG),
@@ -55,6 +58,8 @@ def test_record_and_workspace_sizes():
     f = kv.format_parse("kvarn_k4v2_g128")
     assert kv.record_bytes(f) == 15360
     assert kv.record_bytes(kv.format_parse("kvarn_k8v8_g128")) == 35840
+    assert kv.record_bytes(kv.format_parse("kvarn_k4v2_g64")) == 17408     # + c, s'[2], m'[2] per half
+    assert kv.record_bytes(kv.format_parse("kvarn_k4v2_g32")) == 21504     # + c, s'[4], m'[4] per half
     ws = kv.decode_workspace_bytes(f, 32, 32, 4, 128)
     assert ws > 0 and ws % (132 * 4) == 0   # 132 floats per (seq, q head, split)
     assert kv.decode_workspace_bytes(f, 32, 24, 4, 128) == 0   # G = 6 unsupported
@@ -83,9 +88,13 @@ def test_calls_reject_bad_arguments_before_launch():
     assert L.kvarn_quantize_tiles(fp, 4, 2, dummy, dummy, dummy, dummy, 2 * R + 8, None) == kv.KVARN_E_INVALID_ARG
     assert L.kvarn_quantize_tiles(None, 4, 2, dummy, dummy, dummy, dummy, 2 * R, None) == kv.KVARN_E_INVALID_ARG
     assert L.kvarn_quantize_tiles(fp, 0, 2, None, None, None, None, 0, None) == kv.KVARN_OK   # empty: no work
-    g64 = kv.Format(4, 2, 64, 128, 128, 8)
-    assert L.kvarn_quantize_tiles(ctypes.byref(g64), 4, 2, dummy, dummy, dummy, dummy, 2 * R, None) \
+    g16 = kv.Format(4, 2, 16, 128, 128, 8)
+    assert L.kvarn_quantize_tiles(ctypes.byref(g16), 4, 2, dummy, dummy, dummy, dummy, 2 * R, None) \
         == kv.KVARN_E_UNSUPPORTED
+    # a g64 record is larger: the k4v2 g128 stride is too short for it
+    g64 = kv.format_parse("kvarn_k4v2_g64")
+    assert L.kvarn_quantize_tiles(ctypes.byref(g64), 4, 2, dummy, dummy, dummy, dummy, 2 * R, None) \
+        == kv.KVARN_E_INVALID_ARG
     # append
     assert L.kvarn_append_token(fp, 2, 2, dummy, dummy, None, dummy, dummy, dummy, 4, dummy, 2 * R, None) \
         == kv.KVARN_E_INVALID_ARG
@@ -106,10 +115,11 @@ def test_calls_reject_bad_arguments_before_launch():
     assert dec(ws=ctypes.c_void_p(0x1004)) == kv.KVARN_E_INVALID_ARG
     assert dec(q=None) == kv.KVARN_E_INVALID_ARG
     assert dec(stride=R) == kv.KVARN_E_INVALID_ARG
-    # every bit-width pair of the dtype family decodes
+    # every bit-width pair and group size of the dtype family decodes
     for kb in (2, 4, 8):
         for vb in (2, 4, 8):
-            assert kv.decode_workspace_bytes(kv.format_parse(f"kvarn_k{kb}v{vb}_g128"), 2, 16, 2, 4) > 0
+            for g in (128, 64, 32):
+                assert kv.decode_workspace_bytes(kv.format_parse(f"kvarn_k{kb}v{vb}_g{g}"), 2, 16, 2, 4) > 0
     assert dec(nseq=0) == kv.KVARN_OK
     del args
 

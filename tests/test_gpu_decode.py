@@ -76,7 +76,8 @@ class Setup:
         seqs = list(range(self.B)) if seqs is None else list(seqs)
         _, o64 = oracle.decode_attention(self.fmt.k_bits, self.fmt.v_bits, q[seqs].view(np.uint16), host,
                                          self.stride, self.pt[seqs], self.lens[seqs], self.tail_k[seqs].view(np.uint16),
-                                         self.tail_v[seqs].view(np.uint16), self.sm, self.hkv)
+                                         self.tail_v[seqs].view(np.uint16), self.sm, self.hkv,
+                                         group=self.fmt.group)
         return o64
 
 
@@ -109,6 +110,25 @@ def test_decode_ragged_small_gqa(name, G):
     lens = [326, 128, 5, 0, 1, 1029, 640, 127]
     st = Setup(name, lens, hkv=3, hq=3 * G, seed=25)
     _compare(st.run_gpu(), st.run_oracle(), st.lens)
+
+
+@pytest.mark.parametrize("name", [f"kvarn_k{kb}v{vb}_g{g}" for g in (64, 32) for kb in (2, 4, 8) for vb in (2, 4, 8)])
+@pytest.mark.parametrize("G", [1, 8, 16])
+def test_decode_ragged_small_grouped(name, G):
+    """Quantisation groups of 64 / 32 channels: per-group token scales in the logits and in the PV
+    weights, one page per step."""
+    lens = [326, 128, 5, 0, 1, 1029, 640, 127]
+    st = Setup(name, lens, hkv=2, hq=2 * G, seed=26)
+    _compare(st.run_gpu(), st.run_oracle(), st.lens)
+
+
+def test_decode_grouped_long_sampled():
+    """g32 k4v2 over long contexts (many splits) with tails."""
+    lens = [40000, 16384 + 77, 9000]
+    st = Setup("kvarn_k4v2_g32", lens, hkv=1, hq=8, seed=27, pool_extra=1)
+    out = st.run_gpu()
+    ref = st.run_oracle([0, 1])
+    _compare(out[[0, 1]], ref, st.lens[[0, 1]])
 
 
 def test_decode_special_values():

@@ -38,8 +38,8 @@ def _quantize_gpu(fmt, k16, v16, pages, n_pages_pool, stride=None, canary=None):
     return cache.cpu().numpy(), stride
 
 
-def _ref_half(x16, bits, iters):
-    return oracle.quantize_tile_debug(np.ascontiguousarray(x16).view(np.uint16), bits, iters)
+def _ref_half(x16, bits, iters, group=128):
+    return oracle.quantize_tile_debug(np.ascontiguousarray(x16).view(np.uint16), bits, iters, group=group)
 
 
 def _check_tiles(cache, stride, fmt, k16, v16, pages, tile_heads):
@@ -47,9 +47,10 @@ def _check_tiles(cache, stride, fmt, k16, v16, pages, tile_heads):
     n_bad = 0
     for (i, h) in tile_heads:
         off = int(pages[i]) * stride + h * R
-        rk = _ref_half(k16[i, :, h, :], fmt.k_bits, fmt.sinkhorn_iters)
-        rv = _ref_half(v16[i, :, h, :], fmt.v_bits, fmt.sinkhorn_iters)
-        n_bad += check_record(cache[off:off + R], fmt.k_bits, fmt.v_bits, rk, rv, f"tile {i} head {h}")
+        rk = _ref_half(k16[i, :, h, :], fmt.k_bits, fmt.sinkhorn_iters, fmt.group)
+        rv = _ref_half(v16[i, :, h, :], fmt.v_bits, fmt.sinkhorn_iters, fmt.group)
+        n_bad += check_record(cache[off:off + R], fmt.k_bits, fmt.v_bits, rk, rv, f"tile {i} head {h}",
+                              group=fmt.group)
     assert_code_rate(n_bad, len(tile_heads) * 2 * 128 * 128)
     return n_bad
 
@@ -85,6 +86,18 @@ def test_other_formats(name):
     kt, vt = synth.tiles_view(k), synth.tiles_view(v)
     cache, stride = _quantize_gpu(fmt, kt, vt, [1, 0], 2)
     _check_tiles(cache, stride, fmt, kt, vt, [1, 0], [(0, 0), (0, 1), (1, 0), (1, 1)])
+
+
+@pytest.mark.parametrize("name", [f"kvarn_k{kb}v{vb}_g{g}" for g in (64, 32) for kb in (2, 4, 8) for vb in (2, 4, 8)])
+def test_grouped_formats(name):
+    """Quantisation groups of 64 / 32 channels: per-(token, group) scales, codes and the larger
+    scale block, on 3 tiles x 2 kv heads at permuted pages."""
+    k, v = synth.gen_kv(16, 3 * 128, 2)
+    kt, vt = synth.tiles_view(k), synth.tiles_view(v)
+    fmt = _fmt(name)
+    pages = [2, 0, 1]
+    cache, stride = _quantize_gpu(fmt, kt, vt, pages, 3)
+    _check_tiles(cache, stride, fmt, kt, vt, pages, [(i, h) for i in range(3) for h in range(2)])
 
 
 @pytest.mark.parametrize("iters", [0, 1, 3, 16])
@@ -171,8 +184,9 @@ def test_bulk_full_size_sampled():
 
 # ------------------------------------------------------------------ append
 
-def test_append_fills_like_bulk_quantize():
-    fmt = _fmt("kvarn_k4v2_g128")
+@pytest.mark.parametrize("name", ["kvarn_k4v2_g128", "kvarn_k4v2_g32", "kvarn_k8v4_g64"])
+def test_append_fills_like_bulk_quantize(name):
+    fmt = _fmt(name)
     B, hkv = 2, 2
     R = kv.record_bytes(fmt)
     stride = hkv * R
