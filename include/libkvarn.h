@@ -11,9 +11,10 @@
  *   2. rotate every token along channels with the orthonormal Hadamard matrix Hn = H_128/sqrt(128),
  *   3. balance row (token) and column (channel) RMS by alternating Sinkhorn-style passes in
  *      log space (8 iterations, channels first),
- *   4. quantise each token's 128 channels with asymmetric round-to-nearest at b bits
- *      (keys 4 bits, values 2 bits by default: "kvarn_k4v2_g128"), keeping the scales so that
- *      they can be folded back in when attention reads the cache.
+ *   4. quantise each token's channels with asymmetric round-to-nearest at b bits, in groups of
+ *      g contiguous (rotated) channels (keys 4 bits, values 2 bits, g = 128 by default:
+ *      "kvarn_k4v2_g128"; g = 64 and 32 split a token into 2 or 4 groups), keeping the scales so
+ *      that they can be folded back in when attention reads the cache.
  * The page size equals the tile size and must be 128 ([HYPHO] section "需要关注的几个问题", item 3).
  *
  * Conventions for every call:
@@ -36,11 +37,15 @@
  *                           (nb, gr, nl, half) at ((nb*4 + gr)*16 + nl)*2*U + half*U holds channel
  *                           j = 16*nb + nl for tokens t = 64*half + 16*mb + 4*gr + i (mb, i = 0..3),
  *                           the code of (mb, i) at bit vb*(4*mb + i).
- *   then six float32[128]:  c_K, s'_K, m'_K, c_V, s'_V, m'_V.
- * For a token t of one half, with Y = X Hn, log-scales (u, v) from step 3 and the group
- * statistics mn_t, s_t of Z = Y exp(-u_t - v_j):  c_j = exp(v_j),  s'_t = exp(u_t) s_t,
- * m'_t = exp(u_t) mn_t, and the value read back is  xhat_t = Hn (c ⊙ (m'_t + s'_t q_t)).
- * Record size: 15360 bytes for k4v2, 35840 for k8v8 (vs 65536 for fp16 K+V: 4.27x capacity).
+ *   then the scales, float32: the K half then the V half, each c[128], s'[ng][128], m'[ng][128]
+ *                           with ng = 128 / g groups per token (group gi of token t at [gi][t]);
+ *                           for g = 128 these are six float32[128]: c_K, s'_K, m'_K, c_V, s'_V, m'_V.
+ * For a token t of one half, with Y = X Hn, log-scales (u, v) from step 3 and the statistics
+ * mn_{t,gi}, s_{t,gi} of group gi of Z_t = Y_t exp(-u_t - v):  c_j = exp(v_j),
+ * s'_{t,gi} = exp(u_t) s_{t,gi},  m'_{t,gi} = exp(u_t) mn_{t,gi}, and the value read back is
+ * xhat_t = Hn yhat_t with yhat_tj = c_j (m'_{t,g(j)} + s'_{t,g(j)} q_tj), g(j) = j / g.
+ * Record size: 15360 bytes for k4v2 g128, 17408 for g64, 21504 for g32; 35840 for k8v8 g128
+ * (vs 65536 for fp16 K+V: 4.27x capacity for k4v2 g128).
  */
 #ifndef LIBKVARN_H_
 #define LIBKVARN_H_
@@ -68,8 +73,8 @@ typedef struct {
   int32_t k_bits, v_bits, group, head_dim, block_size, sinkhorn_iters;
 } kvarn_format;
 
-/* Parse a dtype string.  "kvarn_k4v2_g128" -> {4, 2, 128, 128, 128, 8}.  Bits must be 2, 4 or 8;
- * any group other than 128 returns KVARN_E_UNSUPPORTED; malformed strings KVARN_E_INVALID_ARG. */
+/* Parse a dtype string.  "kvarn_k4v2_g128" -> {4, 2, 128, 128, 128, 8}.  Bits must be 2, 4 or 8 and
+ * the group 128, 64 or 32 (else KVARN_E_UNSUPPORTED); malformed strings KVARN_E_INVALID_ARG. */
 kvarn_status kvarn_format_parse(const char* name, kvarn_format* out);
 
 /* Check a format struct filled by hand: same rules as kvarn_format_parse, plus head_dim and

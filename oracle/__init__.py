@@ -54,6 +54,9 @@ def lib():
         L.oracle_decode_attention.restype = i32
         L.oracle_decode_attention.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, i32, vp, vp, vp,
                                               dbl, vp, vp, i32]
+        L.oracle_prefill_attention.restype = i32
+        L.oracle_prefill_attention.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, i32, vp, vp,
+                                               vp, dbl, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -223,3 +226,24 @@ def decode_attention(kb, vb, q, cache, page_stride, page_table, seq_lens, tail_k
                                        float(sm_scale), _p(out), _p(out64), nthreads)
     assert rc == 0
     return out, out64
+
+
+def prefill_attention(kb, vb, q, q_lens, cache, page_stride, page_table, seq_lens, tail_k, tail_v, sm_scale,
+                      num_kv_heads, nthreads=0, group=128, out=None):
+    """q: uint16 [B, max_q, Hq, 128]; query i of sequence s at position seq_lens[s] - q_lens[s] + i attends
+    causally.  -> (out fp16 bits, out fp64), rows i >= q_lens[s] as given in `out` (zeros by default)."""
+    q = _c(q, np.uint16)
+    ql = _c(q_lens, np.int32)
+    cache = _c(cache, np.uint8)
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    tk = _c(tail_k, np.uint16)
+    tv = _c(tail_v, np.uint16)
+    o16 = np.zeros(q.shape, np.uint16) if out is None else np.array(out, np.uint16)
+    o64 = np.zeros(q.shape, np.float64)
+    rc = lib().oracle_prefill_attention(kb, vb, group, q.shape[0], q.shape[1], q.shape[2], num_kv_heads, _p(q),
+                                        _p(ql), _p(cache), page_stride, _p(pt), pt.shape[1], _p(sl), _p(tk), _p(tv),
+                                        float(sm_scale), _p(o16), _p(o64), nthreads)
+    assert rc == 0
+    return o16, o64
+

@@ -567,4 +567,68 @@ int oracle_decode_attention(int kb, int vb, int group, int num_seqs, int num_q_h
   return 0;
 }
 
+// Chunked prefill attention by definition: sequence s holds L = seq_lens[s] tokens (full pages
+// dequantised, tail raw, as for decode) of which the last n = q_lens[s] are this chunk's queries.
+// Query i (i < n) sits at position L - n + i and attends causally to positions 0 .. L - n + i.
+// q, out: [num_seqs][max_q][num_q_heads][128]; rows i >= n of out are left untouched.
+int oracle_prefill_attention(int kb, int vb, int group, int num_seqs, int max_q, int num_q_heads, int num_kv_heads,
+                             const uint16_t* q, const int32_t* q_lens, const uint8_t* cache, int64_t page_stride,
+                             const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens,
+                             const uint16_t* tail_k, const uint16_t* tail_v, double sm_scale, uint16_t* out,
+                             double* out_f64, int nthreads) {
+  if (!fmt_ok(kb, vb, 0, group) || num_seqs < 0 || max_q < 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 1;
+  for (int s = 0; s < num_seqs; ++s)
+    if (q_lens[s] < 0 || q_lens[s] > max_q || q_lens[s] > seq_lens[s]) return 1;
+  const Fmt f{kb, vb, 0, group};
+  const size_t R = record_bytes(f);
+  const int G = num_q_heads / num_kv_heads;
+  parallel_for(static_cast<int64_t>(num_seqs) * num_kv_heads, nthreads, [&](int64_t w) {
+    const int64_t s = w / num_kv_heads;
+    const int h = static_cast<int>(w % num_kv_heads);
+    const int L = seq_lens[s];
+    const int n = q_lens[s];
+    const int full = L / kTok;
+    std::vector<double> K(static_cast<size_t>(L) * kCh), V(static_cast<size_t>(L) * kCh);
+    for (int p = 0; p < full; ++p) {
+      const uint8_t* rec = cache + page_table[s * max_pages_per_seq + p] * page_stride + static_cast<int64_t>(h) * R;
+      dequant_record(f, rec, &K[static_cast<size_t>(p) * kTok * kCh], &V[static_cast<size_t>(p) * kTok * kCh]);
+    }
+    const int64_t tbase = (s * num_kv_heads + h) * static_cast<int64_t>(kTok) * kCh;
+    for (int t = full * kTok; t < L; ++t)
+      for (int j = 0; j < kCh; ++j) {
+        K[static_cast<size_t>(t) * kCh + j] = half_to_double(tail_k[tbase + (t % kTok) * kCh + j]);
+        V[static_cast<size_t>(t) * kCh + j] = half_to_double(tail_v[tbase + (t % kTok) * kCh + j]);
+      }
+    for (int i = 0; i < n; ++i) {
+      const int last = L - n + i;   // causal: keys 0 .. last
+      for (int g = 0; g < G; ++g) {
+        const int hq = h * G + g;
+        const int64_t qo = ((s * max_q + i) * static_cast<int64_t>(num_q_heads) + hq) * kCh;
+        std::vector<double> qq(kCh), logit(last + 1), o(kCh, 0.0);
+        for (int j = 0; j < kCh; ++j) qq[j] = half_to_double(q[qo + j]);
+        double mx = -INFINITY;
+        for (int t = 0; t <= last; ++t) {
+          double d = 0.0;
+          for (int j = 0; j < kCh; ++j) d += qq[j] * K[static_cast<size_t>(t) * kCh + j];
+          logit[t] = sm_scale * d;
+          mx = std::max(mx, logit[t]);
+        }
+        double den = 0.0;
+        for (int t = 0; t <= last; ++t) den += std::exp(logit[t] - mx);
+        for (int t = 0; t <= last; ++t) {
+          const double p = std::exp(logit[t] - mx) / den;
+          for (int j = 0; j < kCh; ++j) o[j] += p * V[static_cast<size_t>(t) * kCh + j];
+        }
+        for (int j = 0; j < kCh; ++j) {
+          if (out) out[qo + j] = double_to_half(o[j]);
+          if (out_f64) out_f64[qo + j] = o[j];
+        }
+      }
+    }
+  });
+  return 0;
+}
+
 }  // extern "C"

@@ -497,3 +497,59 @@ def test_grouped_decode_is_attention_over_the_grouped_dequantisation():
         for h in range(4):
             ref = _attend_np(q[0, h].astype(np.float64), K, V, 0.09)
             np.testing.assert_allclose(o[0, h], ref, rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------ chunked prefill
+
+def test_prefill_is_causal_textbook_attention_over_the_dequantised_cache():
+    # Query i of the chunk sits at position L - n + i and sees keys 0 .. L - n + i: a numpy causal
+    # softmax over the dequantised pages and the raw tail, written independently of the oracle loop.
+    kt, vt = _small_workload(seed=17, n_tiles=2, hkv=2)
+    hkv, hq, B, max_q = 2, 4, 3, 40
+    R = oracle.record_bytes(4, 2)
+    stride = hkv * R
+    cache = np.zeros(3 * stride, np.uint8)
+    oracle.quantize_tiles(4, 2, 8, kt, vt, np.array([2, 0], np.int32), cache, stride)
+    lens = np.array([256 + 30, 128 + 5, 37], np.int32)
+    q_lens = np.array([40, 20, 37], np.int32)      # seq 0: chunk spans page 1 and the tail
+    pt = np.array([[2, 0, 1], [0, 1, 1], [1, 1, 1]], np.int32)
+    rng = np.random.default_rng(18)
+    tail_k = (rng.standard_normal((B, hkv, 128, 128)) * 2).astype(np.float16)
+    tail_v = (rng.standard_normal((B, hkv, 128, 128)) * 2).astype(np.float16)
+    q = rng.standard_normal((B, max_q, hq, 128)).astype(np.float16)
+    sm = 1 / math.sqrt(128)
+    o16, o64 = oracle.prefill_attention(4, 2, q.view(np.uint16), q_lens, cache, stride, pt, lens,
+                                        tail_k.view(np.uint16), tail_v.view(np.uint16), sm, hkv)
+    G = hq // hkv
+    for s in range(B):
+        for h in range(hkv):
+            Ks, Vs = [], []
+            for p in range(lens[s] // 128):
+                rec = cache[pt[s, p] * stride + h * R:pt[s, p] * stride + (h + 1) * R]
+                kh, vh = oracle.dequant_record(4, 2, rec)
+                Ks.append(kh)
+                Vs.append(vh)
+            nt = lens[s] % 128
+            Ks.append(tail_k[s, h, :nt].astype(np.float64))
+            Vs.append(tail_v[s, h, :nt].astype(np.float64))
+            K = np.concatenate(Ks)
+            V = np.concatenate(Vs)
+            lg_all = sm * (q[s, :, h * G:(h + 1) * G].astype(np.float64) @ K.T)     # [max_q, G, L]
+            pos = lens[s] - q_lens[s] + np.arange(max_q)
+            mask = np.arange(lens[s])[None, :] > pos[:, None]                      # [max_q, L]
+            lg_all = np.where(mask[:, None, :], -np.inf, lg_all)
+            P = scipy.special.softmax(lg_all, axis=-1)
+            ref = P @ V                                                             # [max_q, G, 128]
+            for i in range(max_q):
+                if i >= q_lens[s]:
+                    assert np.all(o64[s, i, h * G:(h + 1) * G] == 0)
+                    continue
+                np.testing.assert_allclose(o64[s, i, h * G:(h + 1) * G], ref[i], rtol=1e-10, atol=1e-12)
+    # the chunk's last query sees the whole sequence: the decode oracle's answer
+    last = np.zeros((B, hq, 128), np.float16)
+    for s in range(B):
+        last[s] = q[s, q_lens[s] - 1]
+    _, dec = oracle.decode_attention(4, 2, last.view(np.uint16), cache, stride, pt, lens, tail_k.view(np.uint16),
+                                     tail_v.view(np.uint16), sm, hkv)
+    for s in range(B):
+        np.testing.assert_allclose(o64[s, q_lens[s] - 1], dec[s], rtol=1e-12, atol=1e-14)
