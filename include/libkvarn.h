@@ -137,6 +137,28 @@ kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int
                                     float sm_scale, void* out, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* Chunked prefill attention over the quantised cache: many queries per kv head at once, the phase
+ * before decoding ([HYPHO] section "它怎么做到的：四步流水线" for the cache it reads; scales folded
+ * in on read as for decode, [LEHUY] section "Cơ chế hoạt động", stage 4).
+ * Sequence s holds L = seq_lens[s] tokens (full pages from the cache, the L % 128 newest from the
+ * fp16 tail, as for decode), the last n = q_lens[s] of which are this chunk's queries; their keys
+ * and values must already be in the cache / tail (appended before the call).  Query i < n sits at
+ * position L - n + i and attends causally to positions 0 .. L - n + i:
+ *   out[s][i][hq] = softmax_{t <= L-n+i}(sm_scale * q[s][i][hq] . k_t) V   (fp16)
+ *   q, out    (device) fp16 [num_seqs][max_q][num_q_heads][head_dim]; rows i >= q_lens[s] of out
+ *             are not written
+ *   q_lens    (device) int32 [num_seqs], 0 <= q_lens[s] <= min(max_q, seq_lens[s]) (larger values
+ *             are clamped to that)
+ *   page_table, seq_lens, tail_k, tail_v as for decode.
+ * No workspace.  Supported: one quantisation group per token (g128), query heads per kv head
+ * 1, 2, 4, 8 or 16; other formats return KVARN_E_UNSUPPORTED. */
+kvarn_status kvarn_prefill_attention(const kvarn_format* f, int32_t num_seqs, int32_t max_q,
+                                     int32_t num_q_heads, int32_t num_kv_heads, const void* q,
+                                     const int32_t* q_lens, const void* cache, int64_t page_stride_bytes,
+                                     const int32_t* page_table, int32_t max_pages_per_seq,
+                                     const int32_t* seq_lens, const void* tail_k, const void* tail_v,
+                                     float sm_scale, void* out, hipStream_t stream);
+
 /* Human-readable name of a status. */
 const char* kvarn_status_string(kvarn_status s);
 

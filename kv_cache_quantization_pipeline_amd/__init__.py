@@ -28,6 +28,7 @@ EXPORTS = (
     "kvarn_quantize_tiles",
     "kvarn_append_token",
     "kvarn_decode_attention",
+    "kvarn_prefill_attention",
     "kvarn_status_string",
 )
 
@@ -76,6 +77,9 @@ def lib():
         L.kvarn_decode_attention.restype = i32
         L.kvarn_decode_attention.argtypes = [fp, i32, i32, i32, vp, vp, i64, vp, i32, vp, vp, vp, flt, vp, vp, sz,
                                              vp]
+        L.kvarn_prefill_attention.restype = i32
+        L.kvarn_prefill_attention.argtypes = [fp, i32, i32, i32, i32, vp, vp, vp, i64, vp, i32, vp, vp, vp, flt, vp,
+                                              vp]
         L.kvarn_status_string.restype = ctypes.c_char_p
         L.kvarn_status_string.argtypes = [i32]
         _lib = L
@@ -191,3 +195,30 @@ def decode_attention(fmt: Format, q, cache, page_stride_bytes: int, page_table, 
                                       _ptr(tail_k), _ptr(tail_v), float(sm_scale), _ptr(out), _ptr(workspace),
                                       ws_bytes, _stream(stream))
     _check(st, "kvarn_decode_attention")
+
+
+def prefill_attention(fmt: Format, q, q_lens, cache, page_stride_bytes: int, page_table, seq_lens, tail_k, tail_v,
+                      sm_scale: float, out, num_kv_heads: int, stream=None):
+    """q, out: fp16 [B, max_q, Hq, 128]; q_lens, seq_lens: int32 [B]; page_table int32 [B, max_pages];
+    tails fp16 [B, Hkv, 128, 128].  The last q_lens[s] of the seq_lens[s] cached tokens are the queries."""
+    import torch
+    _need(q, "q", torch.float16, 4)
+    _need(out, "out", torch.float16, 4)
+    _need(q_lens, "q_lens", torch.int32, 1)
+    _need(cache, "cache", torch.uint8)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(tail_k, "tail_k", torch.float16, 4)
+    _need(tail_v, "tail_v", torch.float16, 4)
+    B, max_q, hq = q.shape[0], q.shape[1], q.shape[2]
+    if (out.shape != q.shape or q.shape[3] != 128 or q_lens.shape[0] != B or seq_lens.shape[0] != B
+            or page_table.shape[0] != B):
+        raise ValueError("inconsistent shapes for prefill_attention")
+    if tuple(tail_k.shape) != (B, num_kv_heads, 128, 128) or tail_v.shape != tail_k.shape:
+        raise ValueError(f"tails must be [B, Hkv, 128, 128], got {tuple(tail_k.shape)}")
+    st = lib().kvarn_prefill_attention(ctypes.byref(fmt), B, max_q, hq, num_kv_heads, _ptr(q), _ptr(q_lens),
+                                       _ptr(cache), page_stride_bytes, _ptr(page_table), page_table.shape[1],
+                                       _ptr(seq_lens), _ptr(tail_k), _ptr(tail_v), float(sm_scale), _ptr(out),
+                                       _stream(stream))
+    _check(st, "kvarn_prefill_attention")
+

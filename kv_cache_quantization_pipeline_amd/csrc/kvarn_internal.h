@@ -50,4 +50,13 @@ KVARN_DECL_LAUNCHER(4)
 #undef KVARN_DECL_LAUNCHER
 
 
+// Chunked prefill (one quantisation group per token): grid (num_seqs * num_kv_heads, row blocks of
+// 64 (query token, query head) rows).
+bool prefill_supported(int kb, int vb, int ng, int group_size);
+int prefill_row_blocks(int max_q, int group_size);
+hipError_t launch_prefill(int kb, int vb, int group_size, const _Float16* q, const int32_t* q_lens, int max_q,
+                          const uint8_t* cache, int64_t page_stride, const int32_t* page_table, int max_pages,
+                          const int32_t* seq_lens, const _Float16* tail_k, const _Float16* tail_v, float sm_scale,
+                          _Float16* out, int num_seqs, int num_q_heads, int num_kv_heads, hipStream_t stream);
+
 }  // namespace kvarn

@@ -154,6 +154,33 @@ kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int
                                          stream));
 }
 
+kvarn_status kvarn_prefill_attention(const kvarn_format* f, int32_t num_seqs, int32_t max_q, int32_t num_q_heads,
+                                     int32_t num_kv_heads, const void* q, const int32_t* q_lens, const void* cache,
+                                     int64_t page_stride_bytes, const int32_t* page_table, int32_t max_pages_per_seq,
+                                     const int32_t* seq_lens, const void* tail_k, const void* tail_v, float sm_scale,
+                                     void* out, hipStream_t stream) {
+  const kvarn_status st = check_format(f);
+  if (st != KVARN_OK) return st;
+  if (num_seqs < 0 || max_q < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_pages_per_seq < 0)
+    return KVARN_E_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return KVARN_E_INVALID_ARG;
+  const int G = num_q_heads / num_kv_heads;
+  if (!kvarn::prefill_supported(f->k_bits, f->v_bits, n_groups(f), G)) return KVARN_E_UNSUPPORTED;
+  if (num_seqs == 0 || max_q == 0) return KVARN_OK;
+  if (q == nullptr || q_lens == nullptr || cache == nullptr || page_table == nullptr || seq_lens == nullptr ||
+      tail_k == nullptr || tail_v == nullptr || out == nullptr)
+    return KVARN_E_INVALID_ARG;
+  const int64_t R = record_bytes(f);
+  if (page_stride_bytes < R * num_kv_heads || page_stride_bytes % 16 != 0) return KVARN_E_INVALID_ARG;
+  if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
+  if (kvarn::prefill_row_blocks(max_q, G) > 65535) return KVARN_E_UNSUPPORTED;
+  return hip_status(kvarn::launch_prefill(f->k_bits, f->v_bits, G, static_cast<const _Float16*>(q), q_lens, max_q,
+                                          static_cast<const uint8_t*>(cache), page_stride_bytes, page_table,
+                                          max_pages_per_seq, seq_lens, static_cast<const _Float16*>(tail_k),
+                                          static_cast<const _Float16*>(tail_v), sm_scale, static_cast<_Float16*>(out),
+                                          num_seqs, num_q_heads, num_kv_heads, stream));
+}
+
 const char* kvarn_status_string(kvarn_status s) {
   switch (s) {
     case KVARN_OK:

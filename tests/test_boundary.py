@@ -124,6 +124,25 @@ def test_calls_reject_bad_arguments_before_launch():
     del args
 
 
+def test_prefill_rejects_before_launch():
+    L = kv.lib()
+    f = kv.format_parse("kvarn_k4v2_g128")
+    dummy = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+    R = 15360
+
+    def pre(fmt=f, nseq=2, max_q=4, hq=16, hkv=2, q=dummy, stride=2 * R):
+        return L.kvarn_prefill_attention(ctypes.byref(fmt), nseq, max_q, hq, hkv, q, dummy, dummy, stride, dummy, 4,
+                                         dummy, dummy, dummy, 0.1, dummy, None)
+    assert pre(hq=15) == kv.KVARN_E_INVALID_ARG
+    assert pre(hq=12) == kv.KVARN_E_UNSUPPORTED                      # G = 6
+    assert pre(fmt=kv.format_parse("kvarn_k4v2_g64")) == kv.KVARN_E_UNSUPPORTED   # groups: decode only
+    assert pre(q=None) == kv.KVARN_E_INVALID_ARG
+    assert pre(stride=R) == kv.KVARN_E_INVALID_ARG
+    assert pre(max_q=-1) == kv.KVARN_E_INVALID_ARG
+    assert pre(nseq=0) == kv.KVARN_OK and pre(max_q=0) == kv.KVARN_OK
+    assert pre(max_q=1 << 22, hq=32, hkv=2) == kv.KVARN_E_UNSUPPORTED    # more than 65535 row blocks
+
+
 def test_status_strings():
     assert kv.status_string(0) == "ok"
     assert kv.status_string(3) == "HIP error"
