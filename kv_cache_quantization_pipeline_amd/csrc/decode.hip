@@ -128,8 +128,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   f16x8 ONES;
 #pragma unroll
   for (int sl = 0; sl < 8; ++sl) ONES[sl] = static_cast<_Float16>(1.0f);
-  f16x8 BFAKE = zero8();
-  BFAKE[0] = BFAKE[1] = static_cast<_Float16>(1.0f);
+  f16x8 C0N;
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) C0N[sl] = static_cast<_Float16>(-0.5f * ((1 << VB) - 1));
 
   float m_run = -INFINITY;   // column nl (QK layout)
   float l_part = 0.f;        // this lane's tokens only; rows merged at the end
@@ -198,18 +199,18 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
           if (keperm<KB>(sl) == e8) {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-              const _Float16 hi = static_cast<_Float16>(x[kb]);
-              bqh[kb][sl] = hi;
-              bql[kb][sl] = static_cast<_Float16>(x[kb] - static_cast<float>(hi));
+              const float hi = f16_trunc(x[kb]);
+              bqh[kb][sl] = static_cast<_Float16>(hi);
+              bql[kb][sl] = static_cast<_Float16>(x[kb] - hi);
             }
           }
       } else {
         // k-step e8 / 2 holds code e8 of the four units in slots kg_slot(ui, e8 % 2)
 #pragma unroll
         for (int ui = 0; ui < 4; ++ui) {
-          const _Float16 hi = static_cast<_Float16>(x[ui]);
-          bqh[e8 >> 1][kg_slot<KB>(ui, e8 & 1)] = hi;
-          bql[e8 >> 1][kg_slot<KB>(ui, e8 & 1)] = static_cast<_Float16>(x[ui] - static_cast<float>(hi));
+          const float hi = f16_trunc(x[ui]);
+          bqh[e8 >> 1][kg_slot<KB>(ui, e8 & 1)] = static_cast<_Float16>(hi);
+          bql[e8 >> 1][kg_slot<KB>(ui, e8 & 1)] = static_cast<_Float16>(x[ui] - hi);
         }
       }
     }
@@ -298,12 +299,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
     m_run = m_new;
 
     if constexpr (NG == 1) {
-      // PV weights w_t = p_t s'_t go to the MFMA in fp16.  Their rounding error enters u_j as
-      // sum_t (w~_t - w_t) q_tj; the zero-point term is corrected by -c0 sum_t (w~_t - w_t) with
-      // c0 = (2^b - 1)/2, which centres that error on the codes (q - c0 ~ q + m'/s').
+      // PV weights w_t = p_t s'_t go to the MFMA in fp16 (w~).  u_j = sum_t w_t q_tj + sum_t p_t m'_t
+      // is computed as sum_t w~_t (q_tj - c0) + (sum_t p_t m'_t + c0 sum_t w_t) with c0 = (2^b - 1)/2,
+      // so that the rounding error sum_t (w~_t - w_t)(q_tj - c0) multiplies centred codes; the term
+      // -c0 sum_t w~_t comes from the MFMA itself (weights against a constant operand).
       constexpr float c0 = 0.5f * ((1 << VB) - 1);
       f16x8 aw[4];
-      float msum = 0.f, psum = 0.f, wexact = 0.f, wround = 0.f;
+      float msum = 0.f, psum = 0.f, wexact = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         float wv[2][4];
@@ -324,24 +326,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const _Float16 w0 = static_cast<_Float16>(wv[0][r]);
-          const _Float16 w1 = static_cast<_Float16>(wv[1][r]);
-          aw[kb][vslot<VB>(0, r)] = w0;
-          aw[kb][vslot<VB>(1, r)] = w1;
+          aw[kb][vslot<VB>(0, r)] = static_cast<_Float16>(wv[0][r]);
+          aw[kb][vslot<VB>(1, r)] = static_cast<_Float16>(wv[1][r]);
           wexact += wv[0][r] + wv[1][r];
-          wround += static_cast<float>(w0) + static_cast<float>(w1);
         }
       }
       l_part = l_part * alpha + psum;
-      msum = fmaf(-c0, wround - wexact, msum);
-      // sum_t p_t m'_t enters the PV product as one extra k-step (hi/lo fp16 split)
-      f16x8 afake = zero8();
-      {
-        const _Float16 mh = static_cast<_Float16>(msum);
-        const _Float16 ml = static_cast<_Float16>(msum - static_cast<float>(mh));
-        afake[0] = mh;
-        afake[1] = ml;
-      }
+      // the per-row constant of the PV result: -c0 sum_t w~_t (one MFMA per k-step against -c0) plus
+      // sum_t p_t m'_t + c0 sum_t w_t as one extra k-step (fp16 hi + lo)
+      const f32x4 corr = pv_zero_point<VB>(aw, fmaf(c0, wexact, msum), C0N);
 
       // alpha of the PV rows 4*gr + i lives in lane 4*gr + i (any row of lanes)
       float arow[4];
@@ -357,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
         f32x4 d[P];
 #pragma unroll
         for (int e = 0; e < P; ++e) {
-          d[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+          d[e] = corr;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) d[e] = mfma16(aw[kb], dequant_v<VB>(vc.v[e][nb], kb), d[e]);
         }
@@ -366,7 +359,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
         for (int e = 1; e < P; ++e)
 #pragma unroll
           for (int i = 0; i < 4; ++i) dd[i] = (e_row[i] == e) ? d[e][i] : dd[i];
-        dd = mfma16(afake, BFAKE, dd);
         float cv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) cv[i] = (G >= 4 || i == 0) ? srow[i][3 * 128 + 16 * nb + nl] : cv[0];
@@ -398,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
 #pragma unroll
       for (int gv = 0; gv < NG; ++gv) {
         f16x8 aw[4];
-        float msum = 0.f, wexact = 0.f, wround = 0.f;
+        float msum = 0.f, wexact = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           float wv[2][4];
@@ -418,27 +410,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const _Float16 w0 = static_cast<_Float16>(wv[0][r]);
-            const _Float16 w1 = static_cast<_Float16>(wv[1][r]);
-            aw[kb][vslot<VB>(0, r)] = w0;
-            aw[kb][vslot<VB>(1, r)] = w1;
+            aw[kb][vslot<VB>(0, r)] = static_cast<_Float16>(wv[0][r]);
+            aw[kb][vslot<VB>(1, r)] = static_cast<_Float16>(wv[1][r]);
             wexact += wv[0][r] + wv[1][r];
-            wround += static_cast<float>(w0) + static_cast<float>(w1);
           }
         }
-        msum = fmaf(-c0, wround - wexact, msum);
-        f16x8 afake = zero8();
-        {
-          const _Float16 mh = static_cast<_Float16>(msum);
-          afake[0] = mh;
-          afake[1] = static_cast<_Float16>(msum - static_cast<float>(mh));
-        }
+        const f32x4 corr = pv_zero_point<VB>(aw, fmaf(c0, wexact, msum), C0N);
 #pragma unroll
         for (int nb = EV * gv; nb < EV * gv + EV; ++nb) {
-          f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 d = corr;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) d = mfma16(aw[kb], dequant_v<VB>(vc.v[0][nb], kb), d);
-          d = mfma16(afake, BFAKE, d);
           const float cv = sown[HS + 16 * nb + nl];
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv * d[i]);

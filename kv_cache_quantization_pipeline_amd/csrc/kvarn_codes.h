@@ -282,5 +282,24 @@ __device__ __forceinline__ f16x8 zero8() {
   return f16x8{0, 0, 0, 0, 0, 0, 0, 0};
 }
 
+// Per-row constant of a PV product with fp16 weights aw (A operand, rows = query columns):
+// -c0 sum_k aw[row][k] + m, with m this lane's share of the row's zero-point sum.  c0n is a B
+// operand of -c0 everywhere: against the weights it sums exactly the fp16 weights the PV MFMAs use;
+// against one extra k-step holding -m / c0 as fp16 hi + lo (hi exact, lo its remainder) in slots 0
+// and 1 it adds m.  Every channel of the row gets the same value.
+template <int VB>
+__device__ __forceinline__ f32x4 pv_zero_point(const f16x8 (&aw)[4], float m, f16x8 c0n) {
+  constexpr float c0 = 0.5f * ((1 << VB) - 1);
+  const float x = m * (-1.0f / c0);
+  f16x8 afake = zero8();
+  const float xh = f16_trunc(x);
+  afake[0] = static_cast<_Float16>(xh);
+  afake[1] = static_cast<_Float16>(x - xh);
+  f32x4 c = mfma16(afake, c0n, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) c = mfma16(aw[kb], c0n, c);
+  return c;
+}
+
 }  // namespace
 }  // namespace kvarn

@@ -114,4 +114,11 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// x with its mantissa cut to fp16's 10 bits (rounded toward zero), exact in fp32.  For
+// 2^-14 <= |x| <= 65504 it is an fp16 value, so converting it to fp16 is exact whichever conversion
+// instruction the compiler picks: an fp16 operand and the fp32 value its remainder or rounding error
+// is computed from can then never disagree (two conversion instructions may break rounding ties
+// differently).
+__device__ __forceinline__ float f16_trunc(float x) { return as_f(as_u(x) & 0xFFFFE000u); }
+
 }  // namespace kvarn

@@ -12,7 +12,7 @@
 // MFMA columns of a wave are its 16 query rows.  Per page the wave does what the decode kernel does
 // for one page: QK with the K codes as the A operand and q'' = c_K ⊙ q' (fp16 hi + lo) as the B
 // operand, logits s' (q'' . codes) + m' sigma, the causal mask, an online softmax per row, and PV
-// with the fp16 weights p_t s'_t against the V codes (the zero-point sum added in fp32, channel
+// with the fp16 weights p_t s'_t against the V codes (the zero-point sum as in decode, channel
 // scale c_V on the result).  The fp16 tail is attended in the raw domain: raw q against raw K rows,
 // then the weights against the tail V staged in LDS transposed; that accumulator is added once Hn
 // has been applied to the rotated one.  Only one group per token (g128) is supported here.
@@ -111,6 +111,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
   f16x8 ONES;
 #pragma unroll
   for (int sl = 0; sl < 8; ++sl) ONES[sl] = static_cast<_Float16>(1.0f);
+  f16x8 C0N;
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) C0N[sl] = static_cast<_Float16>(-0.5f * ((1 << VB) - 1));
 
   float m_run = -INFINITY;  // column nl (QK layout)
   float l_part = 0.f;       // this lane's keys only; rows merged at the end
@@ -167,9 +170,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
         if (keperm<KB>(sl) == e8) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
-            const _Float16 hi = static_cast<_Float16>(x[kb]);
-            bqh[kb][sl] = hi;
-            bql[kb][sl] = static_cast<_Float16>(x[kb] - static_cast<float>(hi));
+            const float hi = f16_trunc(x[kb]);
+            bqh[kb][sl] = static_cast<_Float16>(hi);
+            bql[kb][sl] = static_cast<_Float16>(x[kb] - hi);
           }
         }
     }
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
     // PV weights w_t = p_t s'_t go to the MFMA in fp16, divided by the row's largest weight on this
     // page (W) so that none of the weights that matter falls into fp16's subnormal range (small
     // token scales of 8-bit values, spread attention); the row's PV result is multiplied back by W.
-    // The rounding error's zero-point part is corrected as in decode.
+    // The zero-point sum is carried as in decode (codes centred on c0 through one MFMA against -c0).
     constexpr float c0 = 0.5f * ((1 << VB) - 1);
     float wv[8][4];
     float msum = 0.f, psum = 0.f, wmax = 0.f;
@@ -236,38 +239,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
     const float inv_ws = 1.0f / wscale;
     msum *= inv_ws;
     f16x8 aw[4];
-    float wexact = 0.f, wround = 0.f;
+    float wexact = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float x0 = wv[2 * kb][r] * inv_ws, x1 = wv[2 * kb + 1][r] * inv_ws;
-        const _Float16 w0 = static_cast<_Float16>(x0);
-        const _Float16 w1 = static_cast<_Float16>(x1);
-        aw[kb][vslot<VB>(0, r)] = w0;
-        aw[kb][vslot<VB>(1, r)] = w1;
+        aw[kb][vslot<VB>(0, r)] = static_cast<_Float16>(x0);
+        aw[kb][vslot<VB>(1, r)] = static_cast<_Float16>(x1);
         wexact += x0 + x1;
-        wround += static_cast<float>(w0) + static_cast<float>(w1);
       }
     }
     l_part = l_part * alpha + psum;
-    // the row's zero-point sum, added to every channel of its PV result in fp32
-    msum = rows_sum4(fmaf(-c0, wround - wexact, msum));
-    float arow[4], wrow[4], mrow[4];
+    const f32x4 corr = pv_zero_point<VB>(aw, fmaf(c0, wexact, msum), C0N);
+    float arow[4], wrow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       arow[i] = __shfl(alpha, 4 * gr + i);
       wrow[i] = __shfl(wscale, 4 * gr + i);
-      mrow[i] = __shfl(msum, 4 * gr + i);
     }
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      f32x4 d = corr;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) d = mfma16(aw[kb], dequant_v<VB>(vc.v[0][nb], kb), d);
       const float cv = sown[3 * 128 + 16 * nb + nl];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv * wrow[i] * (d[i] + mrow[i]));
+      for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv * wrow[i] * d[i]);
     }
   }
 
