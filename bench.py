@@ -13,6 +13,10 @@ alternately, so each kernel's reads come from HBM, not from the 256 MB Infinity 
 
 Prints one JSON line.  value = algorithmic bytes of the step / step time (GB/s); the per-kernel
 numbers (quantize GB/s, decode tokens/s, fractions of the 8 TB/s HBM peak) are in "kernels".
+
+--variants (a separate run, not the step): the same quantise and decode workloads in the grouped
+formats k4v2 g64 / g32, and chunked prefill (4 sequences, a 512-token chunk on top of 16384 cached
+tokens, 32 query / 4 kv heads, k4v2 g128) against the fp16 MFMA peak; one JSON line of its own.
 """
 import argparse
 import hashlib
@@ -26,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0            # dense fp16 matrix-core peak of MI355X
 FORMAT = "kvarn_k4v2_g128"
 
 # workload sizes (see kv_cache_quantization_pipeline_amd/synth.py WORKLOADS)
@@ -43,6 +48,8 @@ def parse():
                     help="wall seconds per oracle leg (quantise, decode) of the CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for scaling PMC byte counters)")
+    ap.add_argument("--variants", action="store_true",
+                    help="instead of the step: grouped formats (g64, g32) and chunked prefill, one JSON line")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no benchmark: turn the counter_collection.csv files of two rocprofv3 --pmc runs of "
                          "this script (FETCH_SIZE, then WRITE_SIZE; both with --copy-calibration-mib N) into "
@@ -163,6 +170,117 @@ def cpu_baseline(k1, v1, seconds):
             "quantize_GBps": q_bytes / q_time / 1e9, "decode_tokens_per_s": d_calls / d_time}
 
 
+def _events_time(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def variants(args):
+    """Grouped formats and chunked prefill, timed with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import kv_cache_quantization_pipeline_amd as kv
+    from kv_cache_quantization_pipeline_amd import synth
+
+    dev = torch.device("cuda:0")
+    out = {"variants": "grouped formats and chunked prefill", "steps": args.steps, "warmup": args.warmup,
+           "data": "synthetic", "results": {}}
+    res = out["results"]
+    # quantise: the bulk workload, two copies of the inputs
+    w1 = synth.WORKLOADS["bulk_quantize_qwen3_32b_tp2"]
+    k1, v1 = synth.gen_kv(w1["seed"], w1["batch"] * w1["ctx"], w1["n_kv_heads"])
+    kd = [torch.from_numpy(synth.tiles_view(k1)).to(dev)]
+    vd = [torch.from_numpy(synth.tiles_view(v1)).to(dev)]
+    kd.append(kd[0].clone())
+    vd.append(vd[0].clone())
+    del k1, v1
+    pages = torch.from_numpy(synth.gen_page_perm(w1["seed"], Q_TILES)).to(dev)
+    for name in ("kvarn_k4v2_g64", "kvarn_k4v2_g32"):
+        fmt = kv.format_parse(name)
+        R = kv.record_bytes(fmt)
+        caches = [torch.zeros(Q_TILES * Q_HKV * R, dtype=torch.uint8, device=dev) for _ in range(2)]
+        t = _events_time(lambda i: kv.quantize_tiles(fmt, kd[i % 2], vd[i % 2], pages, caches[i % 2], Q_HKV * R),
+                         args.steps, args.warmup)
+        b = Q_TILES * Q_HKV * (2 * 128 * 128 * 2 + R)
+        res[f"quantize_tiles {name}"] = {"us": t * 1e6, "bytes": b, "GBps": b / t / 1e9,
+                                         "frac_hbm": b / t / 1e9 / HBM_PEAK_GBPS}
+        del caches
+    del kd, vd
+
+    # decode: batch 32 x 16384 tokens, 32 query / 4 kv heads, two cache copies
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    pps = D_CTX // 128
+    maxp = pps + 1
+    n_pool = D_B * maxp
+    pt = torch.from_numpy(np.ascontiguousarray(synth.gen_page_perm(2, n_pool).reshape(D_B, maxp))).to(dev)
+    lens = torch.full((D_B,), D_CTX, dtype=torch.int32, device=dev)
+    tk = torch.zeros(D_B, D_HKV, 128, 128, dtype=torch.float16, device=dev)
+    tv = torch.zeros_like(tk)
+    q = torch.from_numpy(synth.gen_q(2, D_B, D_HQ)).to(dev)
+    o = torch.empty_like(q)
+    sm = 1.0 / math.sqrt(128)
+    for name in ("kvarn_k4v2_g64", "kvarn_k4v2_g32"):
+        fmt = kv.format_parse(name)
+        R = kv.record_bytes(fmt)
+        caches = []
+        for _ in range(2):
+            c = torch.zeros(n_pool * D_HKV * R, dtype=torch.uint8, device=dev)
+            for s0 in range(0, D_B, 8):
+                kk = torch.randn(8 * pps, 128, D_HKV, 128, generator=g, device=dev).half()
+                vv = torch.randn(8 * pps, 128, D_HKV, 128, generator=g, device=dev).half()
+                kv.quantize_tiles(fmt, kk, vv, pt[s0:s0 + 8, :pps].reshape(-1).contiguous(), c, D_HKV * R)
+            caches.append(c)
+        ws = torch.empty(kv.decode_workspace_bytes(fmt, D_B, D_HQ, D_HKV, maxp) // 4 + 4, dtype=torch.float32,
+                         device=dev)
+        t = _events_time(lambda i: kv.decode_attention(fmt, q, caches[i % 2], D_HKV * R, pt, lens, tk, tv, sm, o, ws,
+                                                       D_HKV), args.steps, args.warmup)
+        b = D_B * pps * D_HKV * R + D_B * D_HQ * 256 * 2
+        res[f"decode_attention {name}"] = {"us": t * 1e6, "bytes": b, "GBps": b / t / 1e9,
+                                           "frac_hbm": b / t / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": D_B / t}
+        del caches
+
+    # chunked prefill: 4 sequences, 16384 cached tokens + a 512-token chunk (its keys appended), k4v2 g128
+    P_B, P_CTX, P_Q = 4, 16384, 512
+    fmt = kv.format_parse(FORMAT)
+    R = kv.record_bytes(fmt)
+    L = P_CTX + P_Q
+    full = L // 128
+    n_pool = P_B * (full + 1)
+    ptp = torch.from_numpy(np.ascontiguousarray(synth.gen_page_perm(5, n_pool).reshape(P_B, full + 1))).to(dev)
+    cache = torch.zeros(n_pool * D_HKV * R, dtype=torch.uint8, device=dev)
+    for s0 in range(P_B):
+        kk = torch.randn(full, 128, D_HKV, 128, generator=g, device=dev).half()
+        vv = torch.randn(full, 128, D_HKV, 128, generator=g, device=dev).half()
+        kv.quantize_tiles(fmt, kk, vv, ptp[s0, :full].contiguous(), cache, D_HKV * R)
+    plens = torch.full((P_B,), L, dtype=torch.int32, device=dev)
+    qlens = torch.full((P_B,), P_Q, dtype=torch.int32, device=dev)
+    ptk = torch.zeros(P_B, D_HKV, 128, 128, dtype=torch.float16, device=dev)
+    ptv = torch.zeros_like(ptk)
+    pq = torch.randn(P_B, P_Q, D_HQ, 128, generator=g, device=dev).half()
+    po = torch.empty_like(pq)
+    t = _events_time(lambda i: kv.prefill_attention(fmt, pq, qlens, cache, D_HKV * R, ptp, plens, ptk, ptv, sm, po,
+                                                    D_HKV), args.steps, args.warmup)
+    pairs = P_B * D_HQ * (P_Q * (L - P_Q) + P_Q * (P_Q + 1) // 2)   # (query, visible key) pairs
+    flops = 4 * 128 * pairs                                          # QK and PV multiply-adds
+    res["prefill_attention kvarn_k4v2_g128"] = {
+        "us": t * 1e6, "workload": f"{P_B} seqs x ({P_CTX} cached + {P_Q}-token chunk), {D_HQ} q / {D_HKV} kv heads",
+        "flops": flops, "TFLOPs": flops / t / 1e12, "frac_mfma_f16": flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "query_tokens_per_s": P_B * P_Q / t}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -174,6 +292,9 @@ def main():
               "(kv heads and sequences shard independently), so runs with --gpus > 1 are not provided.",
               file=sys.stderr)
         sys.exit(2)
+    if args.variants:
+        variants(args)
+        return
 
     import numpy as np
     import torch
