@@ -94,7 +94,7 @@ kvarn_status kvarn_quantize_tiles(const kvarn_format* f, int32_t num_tiles, int3
   if (k == nullptr || v == nullptr || dst_pages == nullptr || cache == nullptr) return KVARN_E_INVALID_ARG;
   const int64_t R = record_bytes(f);
   if (page_stride_bytes < R * num_kv_heads || page_stride_bytes % 16 != 0) return KVARN_E_INVALID_ARG;
-  if (static_cast<int64_t>(num_tiles) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
+  if (static_cast<int64_t>(num_tiles) * num_kv_heads > 0x3fffffffLL) return KVARN_E_INVALID_ARG;  // 2 WGs each
   return hip_status(kvarn::launch_quantize_tiles(static_cast<const _Float16*>(k), static_cast<const _Float16*>(v),
                                                  dst_pages, static_cast<uint8_t*>(cache), page_stride_bytes, num_tiles,
                                                  num_kv_heads, f->k_bits, f->v_bits, n_groups(f), f->sinkhorn_iters,

@@ -1,7 +1,8 @@
 // KVarN tile quantiser for gfx950.
 //
-// One workgroup of 256 threads (4 waves) handles one tile of one kv head:
-// waves 0-1 the K half, waves 2-3 the V half, each wave 64 of the 128 tokens.
+// One workgroup of 128 threads (2 waves) handles one half (K or V) of one tile
+// of one kv head, each wave 64 of the 128 tokens (the append kernel runs both
+// halves in one 4-wave workgroup: waves 0-1 K, waves 2-3 V).
 // Per tile half ([HYPHO] section "它怎么做到的：四步流水线", steps 1-4;
 // [LEHUY] section "Cơ chế hoạt động: Chuẩn hóa phương sai"):
 //   1. 128-bit loads of the fp16 tile straight into MFMA A operands,
@@ -409,11 +410,10 @@ __device__ __forceinline__ void rotate(const f16x8 (&xa)[4][4], TileRegs& R, int
 template <int KB, int VB, int NG>
 __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ x, int64_t row_stride,
                                                    const _Float16* __restrict__ last_row, uint8_t* __restrict__ rec,
-                                                   int iters, float2 (*xch)[4][64], WaveLds* wlds) {
+                                                   int iters, bool is_v, float2 (*xch)[4][64], WaveLds* wlds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = wave & 1;
-  const bool is_v = wave >= 2;
   const int nl = lane & 15, gr = lane >> 4;
   WaveLds& L = wlds[wave];
   // Every row / column sum starts at kEps: a sum over an all-zero row or column stays positive, its
@@ -549,22 +549,25 @@ __device__ __forceinline__ void quantize_tile_half(const _Float16* __restrict__ 
   }
 }
 
+// One workgroup of 2 waves per (tile, kv head, half): the K and V halves of a tile are independent,
+// so the per-pass barrier only couples the two waves that share a half.
 template <int KB, int VB, int NG>
-__global__ __launch_bounds__(256, 2) void quantize_tiles_kernel(const _Float16* __restrict__ k,
+__global__ __launch_bounds__(128, 2) void quantize_tiles_kernel(const _Float16* __restrict__ k,
                                                                 const _Float16* __restrict__ v,
                                                                 const int32_t* __restrict__ dst_pages,
                                                                 uint8_t* __restrict__ cache, int64_t page_stride,
                                                                 int num_kv_heads, int iters) {
   __shared__ float2 xch[2][4][64];
-  __shared__ WaveLds wlds[4];
-  const int tile = blockIdx.x / num_kv_heads;
-  const int h = blockIdx.x - tile * num_kv_heads;
-  const bool is_v = (threadIdx.x >> 6) >= 2;
+  __shared__ WaveLds wlds[2];
+  const int th = blockIdx.x >> 1;
+  const bool is_v = blockIdx.x & 1;
+  const int tile = th / num_kv_heads;
+  const int h = th - tile * num_kv_heads;
   const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * kCh;
   const _Float16* src = (is_v ? v : k) + (static_cast<int64_t>(tile) * kTok * num_kv_heads + h) * kCh;
   uint8_t* rec = cache + static_cast<int64_t>(dst_pages[tile]) * page_stride +
                  static_cast<int64_t>(h) * record_bytes(KB, VB, NG);
-  quantize_tile_half<KB, VB, NG>(src, row_stride, nullptr, rec, iters, xch, wlds);
+  quantize_tile_half<KB, VB, NG>(src, row_stride, nullptr, rec, iters, is_v, xch, wlds);
 }
 
 // Token append: one workgroup per (sequence, kv head).  Writes the new token into
@@ -600,7 +603,7 @@ __global__ __launch_bounds__(256, 2) void append_kernel(const _Float16* __restri
     const int page = page_table[static_cast<int64_t>(s) * max_pages + (len >> 7)];
     uint8_t* rec =
         cache + static_cast<int64_t>(page) * page_stride + static_cast<int64_t>(h) * record_bytes(KB, VB, NG);
-    quantize_tile_half<KB, VB, NG>(x, kCh, last, rec, iters, xch, wlds);
+    quantize_tile_half<KB, VB, NG>(x, kCh, last, rec, iters, is_v, xch, wlds);
   }
 }
 
@@ -620,7 +623,8 @@ hipError_t launch_quantize_tiles(const _Float16* k, const _Float16* v, const int
   if (num_tiles == 0) return hipSuccess;
 #define KVARN_Q(KB_, VB_, NG_)                                                                                      \
   if (kb == KB_ && vb == VB_ && ng == NG_) {                                                                        \
-    hipLaunchKernelGGL((quantize_tiles_kernel<KB_, VB_, NG_>), dim3(num_tiles * num_kv_heads), dim3(256), 0, stream, \
+    hipLaunchKernelGGL((quantize_tiles_kernel<KB_, VB_, NG_>), dim3(2 * num_tiles * num_kv_heads), dim3(128), 0,    \
+                       stream,                                                                                       \
                        k, v, dst_pages, cache, page_stride, num_kv_heads, iters);                                   \
     return hipGetLastError();                                                                                       \
   }
