@@ -118,10 +118,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   const bool col_ok = e_own < P;
   const int e_oc = col_ok ? e_own : 0;
   // page of the PV result row 4*gr + i held by this lane (one page for all four rows when G >= 4)
+  // (for G >= 4 the four rows of a lane are one page: only index 0 is used then)
   int e_row[4], e_rc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    e_row[i] = (4 * gr + i) / G;
+    e_row[i] = G >= 4 ? (4 * gr) / G : (4 * gr + i) / G;
     e_rc[i] = e_row[i] < P ? e_row[i] : 0;
   }
 
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
       for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * gr + i);
       const float* srow[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) srow[i] = sb + e_rc[i] * SC;
+      for (int i = 0; i < 4; ++i) srow[i] = sb + e_rc[G >= 4 ? 0 : i] * SC;
 
       // PV: one accumulator per page; the lane keeps its rows' page
 #pragma unroll
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
 #pragma unroll
         for (int e = 1; e < P; ++e)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dd[i] = (e_row[i] == e) ? d[e][i] : dd[i];
+          for (int i = 0; i < 4; ++i) dd[i] = (e_row[G >= 4 ? 0 : i] == e) ? d[e][i] : dd[i];
         float cv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) cv[i] = (G >= 4 || i == 0) ? srow[i][3 * 128 + 16 * nb + nl] : cv[0];
@@ -680,7 +681,9 @@ DecodePlan plan_decode(int kb, int vb, int ng, int num_seqs, int num_kv_heads, i
   p.pages_per_group = decode_pages_per_step(kb, vb, ng, group_size);
   const int groups_max = (max_pages_per_seq + p.pages_per_group - 1) / p.pages_per_group;
   const int units = num_seqs * num_kv_heads;
-  const int target_wgs = 512;  // 2 per CU on 256 CUs
+  // 2 workgroups per CU on 256 CUs; 1 per CU with 8-bit codes, whose pages carry 2-3x the bytes
+  // (longer runs per wave pipeline better there: 109 against 118 us for k8v8 at B 32 x 16K)
+  const int target_wgs = (kb == 8 || vb == 8) ? 256 : 512;
   int splits0 = units > 0 ? (target_wgs + units - 1) / units : 1;
   if (splits0 < 1) splits0 = 1;
   int gps = groups_max > 0 ? (groups_max + splits0 - 1) / splits0 : 1;
