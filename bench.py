@@ -7,7 +7,7 @@ One step = one pass of the whole path over one batch of synthetic input:
   2. kvarn_append_token     one new token for each of 32 sequences x 4 kv heads (fp16 tail; a tail that
                             fills is quantised inline)
   3. kvarn_decode_attention decode for 32 sequences at 16384+ tokens, 32 query / 4 kv heads, over the
-                            k4v2 paged cache plus the fp16 tails (decode + combine kernels)
+                            k4v2 paged cache plus the fp16 tails (one kernel: split-K, then the last workgroup merges)
 Inputs are resident in HBM before the timed region.  Two copies of every input and cache are used
 alternately, so each kernel's reads come from HBM, not from the 256 MB Infinity Cache.
 
@@ -113,13 +113,12 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
         q_grid = Q_TILES * Q_HKV * 256
         quant = [v for name, grid, v in rows if "quantize_tiles_kernel" in name and grid == q_grid]
         dec = [v for name, grid, v in rows if "decode_kernel" in name]
-        comb = [v for name, grid, v in rows if "combine_kernel" in name]
-        if not quant or not dec or not comb:
-            raise SystemExit(f"{path}: missing quantize/decode/combine dispatches")
+        if not quant or not dec:
+            raise SystemExit(f"{path}: missing quantize/decode dispatches")
         per.setdefault("quantize_tiles", 0.0)
         per["quantize_tiles"] += sum(quant) / len(quant) * 1024.0 * factor
         per.setdefault("decode_attention", 0.0)
-        per["decode_attention"] += (sum(dec) / len(dec) + sum(comb) / len(comb)) * 1024.0 * factor
+        per["decode_attention"] += sum(dec) / len(dec) * 1024.0 * factor
     out["kernels"] = {k: int(round(v)) for k, v in per.items()}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
@@ -245,8 +244,7 @@ def variants(args):
                 vv = torch.randn(8 * pps, 128, D_HKV, 128, generator=g, device=dev).half()
                 kv.quantize_tiles(fmt, kk, vv, pt[s0:s0 + 8, :pps].reshape(-1).contiguous(), c, D_HKV * R)
             caches.append(c)
-        ws = torch.empty(kv.decode_workspace_bytes(fmt, D_B, D_HQ, D_HKV, maxp) // 4 + 4, dtype=torch.float32,
-                         device=dev)
+        ws = kv.decode_workspace(fmt, D_B, D_HQ, D_HKV, maxp, dev)
         t = _events_time(lambda i: kv.decode_attention(fmt, q, caches[i % 2], D_HKV * R, pt, lens, tk, tv, sm, o, ws,
                                                        D_HKV), args.steps, args.warmup)
         b = D_B * pps * D_HKV * R + D_B * D_HQ * 256 * 2
@@ -349,8 +347,7 @@ def main():
               torch.zeros(D_B, D_HKV, 128, 128, dtype=torch.float16, device=dev)) for _ in range(2)]
     q2 = torch.from_numpy(synth.gen_q(w2["seed"], D_B, D_HQ)).to(dev)
     out2 = torch.empty(D_B, D_HQ, 128, dtype=torch.float16, device=dev)
-    wsb = kv.decode_workspace_bytes(fmt, D_B, D_HQ, D_HKV, max_pages)
-    ws2 = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=dev)
+    ws2 = kv.decode_workspace(fmt, D_B, D_HQ, D_HKV, max_pages, dev)
     sm = 1.0 / math.sqrt(128)
     torch.cuda.synchronize(dev)
     prep_s = time.perf_counter() - t_prep
@@ -430,7 +427,7 @@ def main():
         "append_token": {"us": ta * 1e6, "bytes": app_b, "GBps": app_b / ta / 1e9},
         "decode_attention": {"GBps": dec_b / td / 1e9, "frac_hbm": dec_b / td / 1e9 / HBM_PEAK_GBPS,
                              "us": td * 1e6, "bytes": dec_b, "tokens_per_s": D_B / td,
-                             "note": "decode + combine kernels; one layer call, 1 token per sequence"},
+                             "note": "decode kernel (split-K partials merged by the last workgroup); one layer call, 1 token per sequence"},
     }
     dom = "quantize_tiles" if tq >= td else "decode_attention"
     dk = kernels[dom]

@@ -6,8 +6,7 @@
 //   q . khat_t = s'_t (q'' . q_t) + m'_t sigma,   q' = Hn q, q'' = c_K ⊙ q', sigma = sum_j q''_j
 //   sum_t p_t vhat_t = Hn ( c_V ⊙ ( sum_t (p_t s'_t) q_t + sum_t p_t m'_t ) )
 // so channel scales go into the rotated query, token scales into the logits and
-// the softmax weights, and Hn is applied once, to the merged output (combine
-// kernel).  Logits are kept in the log2 domain (q' is pre-scaled by
+// the softmax weights, and Hn is applied once, to the merged output.  Logits are kept in the log2 domain (q' is pre-scaled by
 // sm_scale * log2 e) so the softmax uses exp2.
 //
 // Work split: grid (sequence * kv head, split), 4 waves per workgroup, each wave
@@ -24,8 +23,12 @@
 // workgroup merges its 4 waves x P streams in LDS and writes one split-K
 // partial per query head.
 //
-// The fp16 tail (the len % 128 newest tokens) and the final inverse rotation
-// are handled by the combine kernel.
+// The fp16 tail (the len % 128 newest tokens) is shared out among the splits of a (sequence,
+// kv head), in raw-domain sums of their partials.  The workgroups of a pair count their arrivals
+// on a device-scope counter in the workspace; the last one to arrive merges the partials and
+// applies the inverse rotation (combine_head), one wave per query head.
+
+#include <algorithm>
 
 #include "kvarn_codes.h"
 #include "kvarn_device.h"
@@ -43,6 +46,164 @@ namespace kvarn {
 namespace {
 
 
+// Stores and loads of the split-K partials that are coherent across the device (the L2 caches of
+// all XCDs) on their own: relaxed atomics at agent scope.  No cache-wide write-back or
+// invalidation is needed around the arrival counter then.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float2 load_agent2(const float* p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Sum over the 64 lanes of x[t] for 16 values t per lane, transposed: lane l returns the sum for
+// t = l & 15 (four exchange-and-add steps that halve the values a lane keeps, then lanes l ^ 16 and
+// l ^ 32).
+__device__ __forceinline__ float transpose_sum16(float (&x)[16], int lane) {
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1) {
+    const bool up = lane & w;
+#pragma unroll
+    for (int i = 0; i < w; ++i) {
+      const float keep = up ? x[w + i] : x[i];
+      const float send = up ? x[i] : x[w + i];
+      x[i] = keep + __shfl_xor(send, w);
+    }
+  }
+  const float y = x[0] + __shfl_xor(x[0], 16);
+  return y + __shfl_xor(y, 32);
+}
+
+// Attention over the fp16 tail (raw domain) for the HW query heads g0, g0 + 4, ... (those below G) of
+// one wave, over n >= 1 tail tokens t0 .. t0+n-1 (n <= 128) of their kv head.  Lane l owns channels
+// 2l, 2l + 1: it reads those two channels of every key and value row (coalesced 256-byte rows) and
+// of each query row, so a head's query costs two registers; the logits are summed across lanes 16
+// tokens at a time (token t of a chunk ends in lanes t, t + 16, t + 32, t + 48).  Rows past the last
+// token are clamped to it (in bounds) and masked.  Per head: mt = max_t lg_t (log2 units;
+// lg = q . k * sm_log2e), lt = sum_t exp2(lg_t - mt), raw = sum_t exp2(lg_t - mt) v_t in the lane's
+// two channels.
+template <int HW, int G>
+__device__ __forceinline__ void tail_heads(const _Float16* __restrict__ q0, int g0, const _Float16* __restrict__ tk,
+                                           const _Float16* __restrict__ tv, int t0, int n, float sm_log2e,
+                                           float (&mt)[HW], float (&lt)[HW], float (&raw)[HW][2], int lane) {
+  constexpr int C = 16;  // tokens per chunk
+  float qx[HW], qy[HW], m[HW];
+#pragma unroll
+  for (int hh = 0; hh < HW; ++hh) {
+    const int g = min(g0 + 4 * hh, G - 1);
+    const f16x2 qq = *reinterpret_cast<const f16x2*>(q0 + g * kCh + 2 * lane);
+    qx[hh] = static_cast<float>(qq[0]) * sm_log2e;
+    qy[hh] = static_cast<float>(qq[1]) * sm_log2e;
+    m[hh] = -INFINITY;
+    lt[hh] = 0.f;
+    raw[hh][0] = raw[hh][1] = 0.f;
+  }
+  // online softmax over the chunks: running max m, sum lt and raw sums rescaled when m grows (the
+  // planner shares the tail out so that a split's share is usually one chunk)
+  for (int c = 0; c < n; c += C) {
+    f16x2 kk[C], vv[C];
+#pragma unroll
+    for (int u = 0; u < C; ++u) {
+      const int row = t0 + min(c + u, n - 1);
+      kk[u] = *reinterpret_cast<const f16x2*>(tk + row * kCh + 2 * lane);
+      vv[u] = *reinterpret_cast<const f16x2*>(tv + row * kCh + 2 * lane);
+    }
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+      float x[C];
+#pragma unroll
+      for (int u = 0; u < C; ++u)
+        x[u] = fmaf(qx[hh], static_cast<float>(kk[u][0]), qy[hh] * static_cast<float>(kk[u][1]));
+      const float d = transpose_sum16(x, lane);
+      const float lg = c + (lane & 15) < n ? d : -INFINITY;
+      float cm = lg;
+#pragma unroll
+      for (int b = 8; b >= 1; b >>= 1) cm = fmaxf(cm, __shfl_xor(cm, b));
+      const float mn = fmaxf(m[hh], cm);
+      const float scale = m[hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hh] - mn);
+      m[hh] = mn;
+      const float p = lg != -INFINITY ? __builtin_amdgcn_exp2f(lg - mn) : 0.f;
+      float ps = p;
+#pragma unroll
+      for (int b = 8; b >= 1; b >>= 1) ps += __shfl_xor(ps, b);
+      lt[hh] = lt[hh] * scale + ps;
+      float w0 = raw[hh][0] * scale, w1 = raw[hh][1] * scale;
+#pragma unroll
+      for (int u = 0; u < C; ++u) {
+        // weight of token c + u: lane u holds it (0 past the last token)
+        const float pw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), u));
+        w0 = fmaf(pw, static_cast<float>(vv[u][0]), w0);
+        w1 = fmaf(pw, static_cast<float>(vv[u][1]), w1);
+      }
+      raw[hh][0] = w0;
+      raw[hh][1] = w1;
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < HW; ++hh) mt[hh] = m[hh];
+}
+
+// Merge the split-K partials of one (sequence, query head), apply Hn once, normalise and store.
+// One wave; lane l owns output channels 2l and 2l + 1.  With M the largest running maximum (log2
+// units) over the splits and f_k = exp2(M_k - M):
+//   L = sum_k f_k L_k,  rot = sum_k f_k rot_k (rotated domain),  raw = sum_k f_k raw_k (the fp16 tail,
+//   raw domain, only in splits that own tail tokens),  out = (Hn rot + raw) / L,
+// all zero for an empty sequence.  part: the n_splits partials of this head.
+__device__ __forceinline__ void combine_head(const float* __restrict__ part, int n_splits, _Float16* __restrict__ o,
+                                             int lane) {
+  float M = -INFINITY;
+  for (int k = lane; k < n_splits; k += 64) M = fmaxf(M, load_agent(part + k * kPartialFloats));
+#pragma unroll
+  for (int b = 32; b >= 1; b >>= 1) M = fmaxf(M, __shfl_xor(M, b));
+
+  float L = 0.f, r[2] = {0.f, 0.f}, w[2] = {0.f, 0.f};
+  if (M != -INFINITY) {
+    // an empty split holds (-inf, 0, 0...): its factor exp2(-inf) is 0
+#pragma unroll 4
+    for (int k = 0; k < n_splits; ++k) {
+      const float* pk = part + k * kPartialFloats;
+      const float2 ml = load_agent2(pk);
+      const float2 fl = load_agent2(pk + 2);
+      const float f = __builtin_amdgcn_exp2f(ml.x - M);
+      L = fmaf(ml.y, f, L);
+      const float2 a = load_agent2(pk + 4 + 2 * lane);
+      r[0] = fmaf(a.x, f, r[0]);
+      r[1] = fmaf(a.y, f, r[1]);
+      if (fl.x != 0.f) {
+        const float2 b = load_agent2(pk + 4 + kCh + 2 * lane);
+        w[0] = fmaf(b.x, f, w[0]);
+        w[1] = fmaf(b.y, f, w[1]);
+      }
+    }
+  }
+  // Hn over the rotated-domain sum: one stage in registers, six across lanes
+  {
+    const float a0 = r[0] + r[1], a1 = r[0] - r[1];
+    r[0] = a0;
+    r[1] = a1;
+  }
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const bool upper = (lane >> b) & 1;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float x = __shfl_xor(r[c], 1 << b);
+      r[c] = upper ? x - r[c] : r[c] + x;
+    }
+  }
+  const float inv_l = L > 0.f ? 1.0f / L : 0.f;
+  constexpr float kInvSqrt128 = 0.08838834764831845f;
+  *reinterpret_cast<f16x2*>(o + 2 * lane) =
+      f16x2{static_cast<_Float16>((r[0] * kInvSqrt128 + w[0]) * inv_l),
+            static_cast<_Float16>((r[1] * kInvSqrt128 + w[1]) * inv_l)};
+}
+
 // Pages per wave step P: the 16 MFMA columns are (page, head) pairs.  G = 16 fills them with one
 // page; otherwise a step is two pages (the most whose codes fit the registers of two waves per
 // SIMD), or one for 8-bit K or V codes, and the columns beyond P*G are masked.
@@ -56,7 +217,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
                                                         int64_t page_stride, const int32_t* __restrict__ page_table,
                                                         int max_pages, const int32_t* __restrict__ seq_lens,
                                                         int num_q_heads, int num_kv_heads, float qscale,
-                                                        float* __restrict__ ws, int n_splits, int groups_per_split) {
+                                                        float* __restrict__ ws, int* __restrict__ counters,
+                                                        int n_splits,
+                                                        const _Float16* __restrict__ tail_k,
+                                                        const _Float16* __restrict__ tail_v, float sm_log2e,
+                                                        _Float16* __restrict__ out) {
   constexpr int P = decode_pages_per_step<KB, VB, G, NG>();
   constexpr int R = record_bytes(KB, VB, NG);
   constexpr int HS = half_scale_floats(NG);   // floats of one half's scales: c, s'[NG], m'[NG]
@@ -64,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   static_assert(NG == 1 || P == 1, "grouped formats take one page per step");
   constexpr int MRG = 130;      // floats per merged row
 
-  __shared__ float qrot[G][kCh];
+  __shared__ __attribute__((aligned(16))) float qrot[G][kCh];
   // Per wave, the scales of the current group and of the next one (P pages each): two stages, so
   // that the next group's scales are copied in while this group is computed.  They are separate
   // arrays, so that the compiler tells the copy into one from the reads of the other.  The final
@@ -141,9 +306,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[nb][i] = 0.f;
 
-  const int gpw = groups_per_split / 4;
-  const int g_begin = sp * groups_per_split + wave * gpw;
-  const int g_end = min(g_begin + gpw, n_groups);
+  // this sequence's groups split evenly over the n_splits workgroups of the pair (the grid is sized
+  // for the longest sequence), then over the 4 waves of each
+  const int gps = (n_groups + n_splits - 1) / n_splits;
+  const int gpw = (gps + 3) / 4;
+  const int s_end = min(sp * gps + gps, n_groups);
+  const int g_begin = sp * gps + wave * gpw;
+  const int g_end = min(g_begin + gpw, s_end);
   const int64_t pt_row = static_cast<int64_t>(s) * max_pages;
   const int64_t head_off = static_cast<int64_t>(h) * R;
 
@@ -466,7 +635,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
 
   // ---- merge the 4 waves x P streams of each head, write one partial per head ----------
   const float l_col = rows_sum4(l_part);
-  __syncthreads();  // the stages are reused below
+  __syncthreads();  // the stages and qrot are reused below
   float* mrg = (wave < 2 ? stage0 : stage1) + (wave & 1) * 16 * MRG;
   if (gr == 0) {
     mrg[nl * MRG + 0] = m_run;
@@ -476,8 +645,36 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) mrg[(4 * gr + i) * MRG + 2 + 16 * nb + nl] = acc[nb][i];
+
+  // This split's share of the fp16 tail (the len % 128 newest tokens): tokens t0 .. t1-1, for the
+  // wave's query heads (wave, wave + 4, ...); raw-domain sums into qrot, (max, sum) into tail_ml.
+  constexpr int HW = (G + 3) / 4;
+  __shared__ float tail_ml[2][G];
+  const int nt = len & (kTok - 1);
+  const int tps = (nt + n_splits - 1) / n_splits;
+  const int t0 = min(nt, sp * tps), t1 = min(nt, t0 + tps);
+  const bool has_tail = t1 > t0;
+  if (has_tail && wave < G) {
+    const int64_t tail_off = static_cast<int64_t>(sh) * kTok * kCh;
+    float tmt[HW], tlt[HW], traw[HW][2];
+    tail_heads<HW, G>(q + (static_cast<int64_t>(s) * num_q_heads + h * G) * kCh, wave, tail_k + tail_off,
+                      tail_v + tail_off, t0, t1 - t0, sm_log2e, tmt, tlt, traw, lane);
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+      const int g = wave + 4 * hh;
+      if (g < G) {
+        qrot[g][2 * lane] = traw[hh][0];
+        qrot[g][2 * lane + 1] = traw[hh][1];
+        if (lane == 0) {
+          tail_ml[0][g] = tmt[hh];
+          tail_ml[1][g] = tlt[hh];
+        }
+      }
+    }
+  }
   __syncthreads();
 
+  // partial of (head g, this split): [M, L, has tail, 0, rot[128], raw[128] (with a tail only)]
   for (int idx = tid; idx < G * kCh; idx += 256) {
     const int g = idx >> 7, j = idx & 127;
     float M = -INFINITY;
@@ -485,7 +682,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
     for (int w = 0; w < 4; ++w)
 #pragma unroll
       for (int e = 0; e < P; ++e) M = fmaxf(M, (w < 2 ? stage0 : stage1)[((w & 1) * 16 + e * G + g) * MRG]);
-    float L = 0.f, A = 0.f;
+    const float mt = has_tail ? tail_ml[0][g] : -INFINITY;
+    M = fmaxf(M, mt);
+    float L = 0.f, A = 0.f, W = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < 4; ++w)
@@ -496,147 +695,52 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
           L = fmaf(row[1], f, L);
           A = fmaf(row[2 + j], f, A);
         }
+      if (has_tail) {
+        const float f = __builtin_amdgcn_exp2f(mt - M);
+        L = fmaf(tail_ml[1][g], f, L);
+        W = qrot[g][j] * f;
+      }
     }
-    float* out = ws + ((static_cast<int64_t>(s) * num_q_heads + h * G + g) * n_splits + sp) * kPartialFloats;
+    float* po = ws + ((static_cast<int64_t>(s) * num_q_heads + h * G + g) * n_splits + sp) * kPartialFloats;
     if (j == 0) {
-      out[0] = M;
-      out[1] = L;
+      store_agent(po, M);
+      store_agent(po + 1, L);
+      store_agent(po + 2, has_tail ? 1.0f : 0.0f);
+      store_agent(po + 3, 0.0f);
     }
-    out[4 + j] = A;
+    store_agent(po + 4 + j, A);
+    if (has_tail) store_agent(po + 4 + kCh + j, W);
   }
-}
 
-// Merge the split-K partials of one (sequence, query head) with its fp16 tail, apply Hn once,
-// normalise.  One workgroup of 256 threads per (sequence, query head); thread (cq, sl) =
-// (tid & 31, tid >> 5) sums channels 4cq .. 4cq+3 over the splits and tail tokens congruent to
-// sl mod 8, so that long contexts (many splits) are merged by all 256 threads.
-__global__ __launch_bounds__(256) void combine_kernel(const _Float16* __restrict__ q, const float* __restrict__ ws,
-                                                     int n_splits, const int32_t* __restrict__ seq_lens,
-                                                     const _Float16* __restrict__ tail_k,
-                                                     const _Float16* __restrict__ tail_v, int num_q_heads,
-                                                     int group_size, float sm_log2e, _Float16* __restrict__ out) {
-  __shared__ float qs[kCh];
-  __shared__ float lg[kTok];
-  __shared__ float red[8][2 * kCh];  // per token/split lane: rotated-domain and tail accumulators
-  __shared__ float wmax[4];
-  __shared__ float lsum[8];
-  const int sq = blockIdx.x;  // s * num_q_heads + query head
-  const int s = sq / num_q_heads;
-  const int hq = sq - s * num_q_heads;
-  const int num_kv_heads = num_q_heads / group_size;
-  const int hk = hq / group_size;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int len = seq_lens[s];
-  const int nt = len & (kTok - 1);
-  const int64_t tail_base = (static_cast<int64_t>(s) * num_kv_heads + hk) * kTok * kCh;
-  const float* part = ws + static_cast<int64_t>(sq) * n_splits * kPartialFloats;
-
-  if (tid < kCh) qs[tid] = static_cast<float>(q[static_cast<int64_t>(sq) * kCh + tid]) * sm_log2e;
+  // ---- the last workgroup of this (sequence, kv head) to finish merges the splits ----------
+  // The partials were stored device-coherent; each thread waits until its stores have completed
+  // before the workgroup counts its arrival, so the workgroup that counts the last arrival finds
+  // every split's partial in place (and reads them device-coherent too).  It sets the counter back
+  // to zero (no other workgroup of this launch touches it any more), so the workspace's counters
+  // are zero again when the launch ends.
+  __shared__ int last_wg;
+  vmcnt_wait<0>();
   __syncthreads();
-  float mx = -INFINITY;
-  if (tid < nt) {
-    const _Float16* kr = tail_k + tail_base + static_cast<int64_t>(tid) * kCh;
-    float d = 0.f;
-    for (int j = 0; j < kCh; j += 8) {
-      const f16x8 kv = *reinterpret_cast<const f16x8*>(kr + j);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) d = fmaf(qs[j + c], static_cast<float>(kv[c]), d);
-    }
-    lg[tid] = d;
-    mx = d;
-  }
-  for (int k = tid; k < n_splits; k += 256) mx = fmaxf(mx, part[k * kPartialFloats]);
-#pragma unroll
-  for (int b = 32; b >= 1; b >>= 1) mx = fmaxf(mx, __shfl_xor(mx, b));
-  if (lane == 0) wmax[wave] = mx;
+  if (tid == 0) last_wg = atomicAdd(counters + sh, 1) == n_splits - 1;
   __syncthreads();
-  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-
-  const int cq = tid & 31, sl = tid >> 5;
-  float ar[4] = {0.f, 0.f, 0.f, 0.f}, aw[4] = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M != -INFINITY) {
-    // an empty split holds (-inf, 0, 0...): its factor exp2(-inf) is 0
-#pragma unroll 4
-    for (int k = sl; k < n_splits; k += 8) {
-      const float* pk = part + k * kPartialFloats;
-      const float f = __builtin_amdgcn_exp2f(pk[0] - M);
-      L = fmaf(pk[1], f, L);
-      const float4 a = *reinterpret_cast<const float4*>(pk + 4 + 4 * cq);
-      ar[0] = fmaf(a.x, f, ar[0]);
-      ar[1] = fmaf(a.y, f, ar[1]);
-      ar[2] = fmaf(a.z, f, ar[2]);
-      ar[3] = fmaf(a.w, f, ar[3]);
-    }
-    for (int t = sl; t < nt; t += 8) {
-      const float f = __builtin_amdgcn_exp2f(lg[t] - M);
-      L += f;
-      const _Float16* vr = tail_v + tail_base + static_cast<int64_t>(t) * kCh + 4 * cq;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) aw[c] = fmaf(f, static_cast<float>(vr[c]), aw[c]);
-    }
+  if (!last_wg) return;
+  if (tid == 0) __hip_atomic_store(counters + sh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int g = wave; g < G; g += 4) {
+    const int64_t sq = static_cast<int64_t>(s) * num_q_heads + h * G + g;
+    combine_head(ws + sq * n_splits * kPartialFloats, n_splits, out + sq * kCh, lane);
   }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    red[sl][4 * cq + c] = ar[c];
-    red[sl][kCh + 4 * cq + c] = aw[c];
-  }
-  if (cq == 0) lsum[sl] = L;
-  __syncthreads();
-  if (wave != 0) return;
-
-  // wave 0: channels 2*lane, 2*lane + 1; Hn over the rotated-domain sum (1 stage in registers,
-  // 6 across lanes), then add the tail and normalise
-  float r[2], w[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    float x = 0.f, y = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      x += red[k][2 * lane + c];
-      y += red[k][kCh + 2 * lane + c];
-    }
-    r[c] = x;
-    w[c] = y;
-  }
-  float Lt = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) Lt += lsum[k];
-  {
-    const float a0 = r[0] + r[1], a1 = r[0] - r[1];
-    r[0] = a0;
-    r[1] = a1;
-  }
-#pragma unroll
-  for (int b = 0; b < 6; ++b) {
-    const bool upper = (lane >> b) & 1;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const float o = __shfl_xor(r[c], 1 << b);
-      r[c] = upper ? o - r[c] : r[c] + o;
-    }
-  }
-  const float inv_l = Lt > 0.f ? 1.0f / Lt : 0.f;
-  constexpr float kInvSqrt128 = 0.08838834764831845f;
-  _Float16* o = out + static_cast<int64_t>(sq) * kCh + 2 * lane;
-  o[0] = static_cast<_Float16>((r[0] * kInvSqrt128 + w[0]) * inv_l);
-  o[1] = static_cast<_Float16>((r[1] * kInvSqrt128 + w[1]) * inv_l);
 }
 
 template <int KB, int VB, int G, int NG>
 static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64_t page_stride,
                                   const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                                   const _Float16* tail_k, const _Float16* tail_v, float sm_scale, _Float16* out,
-                                  float* workspace, int num_seqs, int num_q_heads, int num_kv_heads,
+                                  float* workspace, int* counters, int num_seqs, int num_q_heads, int num_kv_heads,
                                   const DecodePlan& plan, hipStream_t stream) {
   const float qscale = sm_scale * kLog2e * 0.08838834764831845f;
   hipLaunchKernelGGL((decode_kernel<KB, VB, G, NG>), dim3(num_seqs * num_kv_heads, plan.n_splits), dim3(256), 0, stream,
                      q, cache, page_stride, page_table, max_pages, seq_lens, num_q_heads, num_kv_heads, qscale,
-                     workspace, plan.n_splits, plan.groups_per_split);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(num_seqs * num_q_heads), dim3(256), 0, stream, q, workspace, plan.n_splits,
-                     seq_lens, tail_k, tail_v, num_q_heads, G, sm_scale * kLog2e, out);
+                     workspace, counters, plan.n_splits, tail_k, tail_v, sm_scale * kLog2e, out);
   return hipGetLastError();
 }
 
@@ -647,14 +751,14 @@ static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64
 hipError_t KVARN_LAUNCHER_NAME(KVARN_DECODE_NG)(int kb, int vb, int group_size, const _Float16* q, const uint8_t* cache,
                                                int64_t page_stride, const int32_t* page_table, int max_pages,
                                                const int32_t* seq_lens, const _Float16* tail_k, const _Float16* tail_v,
-                                               float sm_scale, _Float16* out, float* workspace, int num_seqs,
+                                               float sm_scale, _Float16* out, float* workspace, int* counters, int num_seqs,
                                                int num_q_heads, int num_kv_heads, const DecodePlan& plan,
                                                hipStream_t stream) {
   constexpr int NG = KVARN_DECODE_NG;
 #define KVARN_DECODE_CASE(KB_, VB_, G_)                                                                           \
   if (kb == KB_ && vb == VB_ && group_size == G_)                                                                 \
     return launch_decode_t<KB_, VB_, G_, NG>(q, cache, page_stride, page_table, max_pages, seq_lens, tail_k, tail_v, \
-                                             sm_scale, out, workspace, num_seqs, num_q_heads, num_kv_heads, plan,  \
+                                             sm_scale, out, workspace, counters, num_seqs, num_q_heads, num_kv_heads, plan,  \
                                              stream);
 #define KVARN_DECODE_BITS(G_)                                                                               \
   KVARN_DECODE_CASE(2, 2, G_) KVARN_DECODE_CASE(2, 4, G_) KVARN_DECODE_CASE(2, 8, G_)                       \
@@ -686,11 +790,12 @@ DecodePlan plan_decode(int kb, int vb, int ng, int num_seqs, int num_kv_heads, i
   const int target_wgs = (kb == 8 || vb == 8) ? 256 : 512;
   int splits0 = units > 0 ? (target_wgs + units - 1) / units : 1;
   if (splits0 < 1) splits0 = 1;
-  int gps = groups_max > 0 ? (groups_max + splits0 - 1) / splits0 : 1;
-  gps = ((gps + 3) / 4) * 4;  // whole groups per wave
-  if (gps < 4) gps = 4;
+  const int gps = groups_max > 0 ? (groups_max + splits0 - 1) / splits0 : 1;
   p.groups_per_split = gps;
   p.n_splits = groups_max > 0 ? (groups_max + gps - 1) / gps : 1;
+  // the fp16 tail (up to 127 tokens) is shared out among the splits: at least 8 of them where the
+  // grid has room, so that a split's share is one 16-token chunk
+  p.n_splits = std::max(p.n_splits, std::min(8, splits0));
   return p;
 }
 
@@ -702,13 +807,13 @@ bool decode_supported(int kb, int vb, int ng, int group_size) {
 hipError_t launch_decode(int kb, int vb, int ng, int group_size, const _Float16* q, const uint8_t* cache,
                          int64_t page_stride, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                          const _Float16* tail_k, const _Float16* tail_v, float sm_scale, _Float16* out,
-                         float* workspace, int num_seqs, int num_q_heads, int num_kv_heads, const DecodePlan& plan,
+                         float* workspace, int* counters, int num_seqs, int num_q_heads, int num_kv_heads, const DecodePlan& plan,
                          hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
   auto* fn = ng == 1 ? launch_decode_ng1 : ng == 2 ? launch_decode_ng2 : ng == 4 ? launch_decode_ng4 : nullptr;
   if (fn == nullptr) return hipErrorInvalidValue;
   return fn(kb, vb, group_size, q, cache, page_stride, page_table, max_pages, seq_lens, tail_k, tail_v, sm_scale, out,
-            workspace, num_seqs, num_q_heads, num_kv_heads, plan, stream);
+            workspace, counters, num_seqs, num_q_heads, num_kv_heads, plan, stream);
 }
 #endif
 

@@ -16,8 +16,9 @@ hipError_t launch_append(const _Float16* k_new, const _Float16* v_new, int32_t* 
                          int64_t page_stride, int num_seqs, int num_kv_heads, int kb, int vb, int ng, int iters,
                          hipStream_t stream);
 
-// Split-K decode plan: the grid is (num_seqs*num_kv_heads, n_splits) workgroups of 4 waves;
-// a split covers groups_per_split groups of pages_per_group pages, groups_per_split / 4 per wave.
+// Split-K decode plan: the grid is (num_seqs*num_kv_heads, n_splits) workgroups of 4 waves, n_splits
+// sized for max_pages_per_seq (groups_per_split groups of pages_per_group pages per split at that
+// length).  The kernel shares each sequence's actual groups evenly among its n_splits workgroups.
 struct DecodePlan {
   int pages_per_group;
   int groups_per_split;
@@ -27,23 +28,30 @@ struct DecodePlan {
 int decode_pages_per_step(int kb, int vb, int ng, int group_size);
 DecodePlan plan_decode(int kb, int vb, int ng, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq);
 
-// Workspace floats per (sequence, query head, split): running max, running sum, two pad floats
-// (16-byte alignment of what follows), 128 accumulators.
-constexpr int kPartialFloats = 132;
+// Decode workspace: one int32 arrival counter per (sequence, kv head), padded to 256 bytes, then
+// kPartialFloats floats per (sequence, query head, split): running max, running sum, a flag (1 if
+// the split owns fp16 tail tokens), a pad float, 128 rotated-domain accumulators and 128 raw-domain
+// tail accumulators (written only with the flag set).  The counters must be zero when a launch
+// starts; every launch leaves them zero.
+constexpr int kPartialFloats = 260;
+inline size_t decode_counter_bytes(int num_seqs, int num_kv_heads) {
+  return (static_cast<size_t>(num_seqs) * num_kv_heads * sizeof(int32_t) + 255) / 256 * 256;
+}
 
 bool decode_supported(int kb, int vb, int ng, int group_size);
 
-hipError_t launch_decode(int kb, int vb, int ng, int group_size, const _Float16* q, const uint8_t* cache, int64_t page_stride,
-                         const int32_t* page_table, int max_pages, const int32_t* seq_lens, const _Float16* tail_k,
-                         const _Float16* tail_v, float sm_scale, _Float16* out, float* workspace, int num_seqs,
-                         int num_q_heads, int num_kv_heads, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_decode(int kb, int vb, int ng, int group_size, const _Float16* q, const uint8_t* cache,
+                         int64_t page_stride, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                         const _Float16* tail_k, const _Float16* tail_v, float sm_scale, _Float16* out,
+                         float* workspace, int* counters, int num_seqs, int num_q_heads, int num_kv_heads,
+                         const DecodePlan& plan, hipStream_t stream);
 // The kernels of one group count (ng = 1, 2, 4), each in its own object.
-#define KVARN_DECL_LAUNCHER(N)                                                                                       \
-  hipError_t launch_decode_ng##N(int kb, int vb, int group_size, const _Float16* q, const uint8_t* cache,            \
-                                 int64_t page_stride, const int32_t* page_table, int max_pages,                      \
-                                 const int32_t* seq_lens, const _Float16* tail_k, const _Float16* tail_v,            \
-                                 float sm_scale, _Float16* out, float* workspace, int num_seqs, int num_q_heads,     \
-                                 int num_kv_heads, const DecodePlan& plan, hipStream_t stream);
+#define KVARN_DECL_LAUNCHER(N)                                                                                \
+  hipError_t launch_decode_ng##N(int kb, int vb, int group_size, const _Float16* q, const uint8_t* cache,     \
+                                 int64_t page_stride, const int32_t* page_table, int max_pages,               \
+                                 const int32_t* seq_lens, const _Float16* tail_k, const _Float16* tail_v,     \
+                                 float sm_scale, _Float16* out, float* workspace, int* counters, int num_seqs, \
+                                 int num_q_heads, int num_kv_heads, const DecodePlan& plan, hipStream_t stream);
 KVARN_DECL_LAUNCHER(1)
 KVARN_DECL_LAUNCHER(2)
 KVARN_DECL_LAUNCHER(4)

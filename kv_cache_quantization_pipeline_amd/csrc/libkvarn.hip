@@ -81,7 +81,8 @@ size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int
   if (!kvarn::decode_supported(f->k_bits, f->v_bits, n_groups(f), G)) return 0;
   const kvarn::DecodePlan plan =
       kvarn::plan_decode(f->k_bits, f->v_bits, n_groups(f), num_seqs, num_kv_heads, G, max_pages_per_seq);
-  return static_cast<size_t>(num_seqs) * num_q_heads * plan.n_splits * kvarn::kPartialFloats * sizeof(float);
+  return kvarn::decode_counter_bytes(num_seqs, num_kv_heads) +
+         static_cast<size_t>(num_seqs) * num_q_heads * plan.n_splits * kvarn::kPartialFloats * sizeof(float);
 }
 
 kvarn_status kvarn_quantize_tiles(const kvarn_format* f, int32_t num_tiles, int32_t num_kv_heads, const void* k,
@@ -150,7 +151,9 @@ kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int
                                          static_cast<const uint8_t*>(cache), page_stride_bytes, page_table,
                                          max_pages_per_seq, seq_lens, static_cast<const _Float16*>(tail_k),
                                          static_cast<const _Float16*>(tail_v), sm_scale, static_cast<_Float16*>(out),
-                                         static_cast<float*>(workspace), num_seqs, num_q_heads, num_kv_heads, plan,
+                                         reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                                  kvarn::decode_counter_bytes(num_seqs, num_kv_heads)),
+                                         static_cast<int*>(workspace), num_seqs, num_q_heads, num_kv_heads, plan,
                                          stream));
 }
 

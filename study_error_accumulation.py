@@ -126,8 +126,7 @@ def run(args, seed):
             self.lens = torch.full((1,), args.prefix, dtype=torch.int32, device=dev)
             self.tk = torch.zeros(1, HKV, 128, D, dtype=torch.float16, device=dev)
             self.tv = torch.zeros_like(self.tk)
-            wsb = kv.decode_workspace_bytes(self.fmt, 1, HQ, HKV, self.maxp)
-            self.ws = torch.empty(max(wsb, 16) // 4 + 4, dtype=torch.float32, device=dev)
+            self.ws = kv.decode_workspace(self.fmt, 1, HQ, HKV, self.maxp, dev)
             self.x = x0.clone()
 
         def attend(self, q, k, v):

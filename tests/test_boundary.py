@@ -61,7 +61,10 @@ def test_record_and_workspace_sizes():
     assert kv.record_bytes(kv.format_parse("kvarn_k4v2_g64")) == 17408     # + c, s'[2], m'[2] per half
     assert kv.record_bytes(kv.format_parse("kvarn_k4v2_g32")) == 21504     # + c, s'[4], m'[4] per half
     ws = kv.decode_workspace_bytes(f, 32, 32, 4, 128)
-    assert ws > 0 and ws % (132 * 4) == 0   # 132 floats per (seq, q head, split)
+    # 32 x 4 int32 arrival counters (512 B, a multiple of 256), then 260 floats per (seq, q head, split)
+    assert ws > 512 and (ws - 512) % (32 * 32 * 260 * 4) == 0
+    # 9 counters padded to 256 B; one page, but the fp16 tail is shared out among 8 splits
+    assert kv.decode_workspace_bytes(f, 3, 3, 3, 1) == 256 + 3 * 3 * 8 * 260 * 4
     assert kv.decode_workspace_bytes(f, 32, 24, 4, 128) == 0   # G = 6 unsupported
     for G in (1, 2, 4, 8, 16):
         assert kv.decode_workspace_bytes(f, 4, 2 * G, 2, 16) > 0

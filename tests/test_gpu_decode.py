@@ -55,13 +55,13 @@ class Setup:
         self.q = synth.gen_q(seed, self.B, hq)
         self.sm = 1.0 / math.sqrt(128)
 
-    def run_gpu(self, pt=None, cache=None, max_pages=None, q=None):
+    def run_gpu(self, pt=None, cache=None, max_pages=None, q=None, ws=None):
         pt = self.pt if pt is None else pt
         cache = self.cache if cache is None else cache
         q = self.q if q is None else q
         mp = pt.shape[1]
-        wsb = kv.decode_workspace_bytes(self.fmt, self.B, self.hq, self.hkv, mp)
-        ws = torch.empty(max(wsb, 16) // 4 + 4, dtype=torch.float32, device=DEV)
+        if ws is None:
+            ws = kv.decode_workspace(self.fmt, self.B, self.hq, self.hkv, mp, DEV)
         out = torch.empty(self.B, self.hq, 128, dtype=torch.float16, device=DEV)
         kv.decode_attention(self.fmt, torch.from_numpy(q).to(DEV), cache, self.stride,
                             torch.from_numpy(np.ascontiguousarray(pt)).to(DEV), torch.from_numpy(self.lens).to(DEV),
@@ -200,3 +200,26 @@ def test_decode_long_context_sampled():
     out = st.run_gpu()
     ref = st.run_oracle([1, 2])
     _compare(out[[1, 2]], ref, st.lens[[1, 2]])
+
+
+def test_workspace_counters_return_to_zero():
+    """The workspace opens with one arrival counter per (sequence, kv head); the last split-K
+    workgroup of a pair resets it, so after every call the counters are zero and one workspace
+    serves later calls of other shapes and formats, with results identical to a fresh workspace."""
+    a = Setup("kvarn_k4v2_g128", [1029, 5, 0, 640, 3000], hkv=2, hq=16, seed=31)
+    b = Setup("kvarn_k8v4_g64", [300, 129, 2000], hkv=3, hq=3, seed=32)
+    need = max(kv.decode_workspace_bytes(a.fmt, a.B, a.hq, a.hkv, a.pt.shape[1]),
+               kv.decode_workspace_bytes(b.fmt, b.B, b.hq, b.hkv, b.pt.shape[1]))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    n_cnt = max(a.B * a.hkv, b.B * b.hkv)
+    first = a.run_gpu(ws=ws)
+    assert torch.all(ws[:4 * n_cnt].view(torch.int32) == 0).item()
+    other = b.run_gpu(ws=ws)
+    assert torch.all(ws[:4 * n_cnt].view(torch.int32) == 0).item()
+    again = a.run_gpu(ws=ws)
+    assert torch.all(ws[:4 * n_cnt].view(torch.int32) == 0).item()
+    assert np.array_equal(first.view(np.uint16), again.view(np.uint16))
+    assert np.array_equal(first.view(np.uint16), a.run_gpu().view(np.uint16))
+    assert np.array_equal(other.view(np.uint16), b.run_gpu().view(np.uint16))
+    _compare(first, a.run_oracle(), a.lens)
+    _compare(other, b.run_oracle(), b.lens)

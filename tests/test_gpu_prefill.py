@@ -111,8 +111,7 @@ def test_prefill_last_query_equals_decode():
     st = Prefill("kvarn_k4v2_g128", [1029, 326, 640], [77, 40, 64], hkv=2, hq=16, seed=33)
     pre = st.run_gpu()
     q_last = np.stack([st.q[s, st.q_lens[s] - 1] for s in range(st.B)])
-    wsb = kv.decode_workspace_bytes(st.fmt, st.B, st.hq, st.hkv, st.max_pages)
-    ws = torch.empty(max(wsb, 16) // 4 + 4, dtype=torch.float32, device=DEV)
+    ws = kv.decode_workspace(st.fmt, st.B, st.hq, st.hkv, st.max_pages, DEV)
     dec = torch.empty(st.B, st.hq, 128, dtype=torch.float16, device=DEV)
     kv.decode_attention(st.fmt, torch.from_numpy(q_last).to(DEV), st.cache, st.stride,
                         torch.from_numpy(st.pt).to(DEV), torch.from_numpy(st.lens).to(DEV),

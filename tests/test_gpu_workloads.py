@@ -28,8 +28,7 @@ DEV = "cuda"
 
 def _decode(fmt, q, cache, stride, pt, lens, tk, tv, sm, hkv):
     B, hq = q.shape[0], q.shape[1]
-    wsb = kv.decode_workspace_bytes(fmt, B, hq, hkv, pt.shape[1])
-    ws = torch.empty(max(wsb, 16) // 4 + 4, dtype=torch.float32, device=DEV)
+    ws = kv.decode_workspace(fmt, B, hq, hkv, pt.shape[1], DEV)
     out = torch.empty(B, hq, 128, dtype=torch.float16, device=DEV)
     kv.decode_attention(fmt, q, cache, stride, pt, lens, tk, tv, sm, out, ws, hkv)
     return out
