@@ -15,8 +15,11 @@ Prints one JSON line.  value = algorithmic bytes of the step / step time (GB/s);
 numbers (quantize GB/s, decode tokens/s, fractions of the 8 TB/s HBM peak) are in "kernels".
 
 --variants (a separate run, not the step): the same quantise and decode workloads in the grouped
-formats k4v2 g64 / g32, and chunked prefill (4 sequences, a 512-token chunk on top of 16384 cached
-tokens, 32 query / 4 kv heads, k4v2 g128) against the fp16 MFMA peak; one JSON line of its own.
+formats k4v2 g64 / g32; chunked prefill (4 sequences, a 512-token chunk on top of 16384 cached
+tokens, 32 query / 4 kv heads, k4v2 g128) against the fp16 MFMA peak; the long-context serving loop
+(4 sequences x 128K tokens, 8 query / 1 kv head, append + decode per step, five cache copies in turn);
+and the ragged continuous-batching step (64 sequences of 1K-32K tokens, k4v2 and k8v8 pools); one JSON
+line of its own.
 """
 import argparse
 import hashlib
@@ -279,7 +282,205 @@ def variants(args):
         "us": t * 1e6, "workload": f"{P_B} seqs x ({P_CTX} cached + {P_Q}-token chunk), {D_HQ} q / {D_HKV} kv heads",
         "flops": flops, "TFLOPs": flops / t / 1e12, "frac_mfma_f16": flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS,
         "query_tokens_per_s": P_B * P_Q / t}
+    del cache, ptk, ptv, pq, po
+    res["decode_step long_context"] = long_context_steps(kv, synth, dev)
+    res["decode_step ragged_mixed"] = ragged_mixed_steps(kv, synth, dev, args.steps)
     print(json.dumps(out), flush=True)
+
+
+def _append_bytes(lens_before, n_kv_heads, R):
+    """Algorithmic bytes of one append call: new K/V rows read, tail slots written, lengths read and
+    written; a tile that fills is read (K and V, 128 x 128 fp16) and its record written."""
+    n = len(lens_before)
+    fills = int(((lens_before + 1) % 128 == 0).sum())
+    return n * n_kv_heads * 4 * 256 + n * 8 + fills * n_kv_heads * (2 * 128 * 128 * 2 + R)
+
+
+def _decode_bytes(lens, n_kv_heads, n_q_heads, R):
+    """Algorithmic bytes of one decode call: full pages, fp16 tails (K and V rows), queries and outputs."""
+    return int((lens // 128 * n_kv_heads * R).sum() + (lens % 128 * n_kv_heads * 512).sum()
+               + len(lens) * n_q_heads * 256 * 2)
+
+
+def long_context_steps(kv, synth, dev):
+    """4 sequences x 131072 tokens, 8 query heads on 1 kv head, k4v2: 128 steps of append one token +
+    decode per copy (the last append of each copy fills the tail and quantises it inline).  The cache
+    is 63 MB, so five independent copies (315 MB) are used in turn and every read comes from HBM,
+    not from the 256 MB Infinity Cache.  Timed with HIP events on the launch stream around each call;
+    the calls are prepared (marshalled once), so that the host keeps ahead of the GPU."""
+    import numpy as np
+    import torch
+    w = synth.WORKLOADS["decode_long_b4_ctx128k"]
+    fmt = kv.format_parse(FORMAT)
+    R = kv.record_bytes(fmt)
+    B, hq, hkv, ctx = w["batch"], w["n_q_heads"], w["n_kv_heads"], w["ctx"]
+    full, n_copies, n_steps = ctx // 128, 5, 128
+    maxp = full + 1
+    stride = hkv * R
+    pt = torch.from_numpy(synth.gen_page_perm(w["seed"], B * maxp).reshape(B, maxp)).to(dev)
+    dst = pt[:, :full].reshape(-1).contiguous()
+    k, v = synth.gen_kv(w["seed"], B * full * 128, hkv)
+    kd, vd = torch.from_numpy(synth.tiles_view(k)).to(dev), torch.from_numpy(synth.tiles_view(v)).to(dev)
+    del k, v
+    caches = []
+    for _ in range(n_copies):
+        c = torch.zeros(B * maxp * stride, dtype=torch.uint8, device=dev)
+        kv.quantize_tiles(fmt, kd, vd, dst, c, stride)
+        caches.append(c)
+    del kd, vd
+    rng = np.random.default_rng(w["seed"] + 7)
+    knew = torch.from_numpy((rng.standard_normal((n_steps, B, hkv, 128)) * 1.5).astype(np.float16)).to(dev)
+    vnew = torch.from_numpy((rng.standard_normal((n_steps, B, hkv, 128)) * 1.5).astype(np.float16)).to(dev)
+    q = torch.from_numpy(synth.gen_q(w["seed"], B, hq)).to(dev)
+    out = torch.empty(B, hq, 128, dtype=torch.float16, device=dev)
+    lens = [torch.full((B,), ctx, dtype=torch.int32, device=dev) for _ in range(n_copies)]
+    tails = [(torch.zeros(B, hkv, 128, 128, dtype=torch.float16, device=dev),
+              torch.zeros(B, hkv, 128, 128, dtype=torch.float16, device=dev)) for _ in range(n_copies)]
+    ws = kv.decode_workspace(fmt, B, hq, hkv, maxp, dev)
+    sm = 1.0 / math.sqrt(128)
+
+    # the calls marshalled once (the GPU work per call is a few microseconds, so the host must not
+    # fall behind), and the events created beforehand
+    apps = [[kv.prepare_append_token(fmt, knew[s], vnew[s], lens[c], tails[c][0], tails[c][1], pt, caches[c], stride)
+             for c in range(n_copies)] for s in range(n_steps)]
+    decs = [kv.prepare_decode_attention(fmt, q, caches[c], stride, pt, lens[c], tails[c][0], tails[c][1], sm, out, ws,
+                                        hkv) for c in range(n_copies)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps * n_copies)]
+
+    def run(steps, record):
+        ev = []
+        for s in range(steps):
+            for c in range(n_copies):
+                e = events[s * n_copies + c]
+                if record:
+                    e[0].record()
+                apps[s][c]()
+                if record:
+                    e[1].record()
+                decs[c]()
+                if record:
+                    e[2].record()
+                    ev.append(e)
+        return ev
+
+    run(4, False)                                  # warm-up, then back to the starting state
+    torch.cuda.synchronize(dev)
+    for c in range(n_copies):
+        lens[c].fill_(ctx)
+        tails[c][0].zero_()
+        tails[c][1].zero_()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    ev = run(n_steps, True)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    assert lens[0].cpu().tolist() == [ctx + n_steps] * B
+    n = len(ev)
+    ta = sum(e[0].elapsed_time(e[1]) for e in ev) / n * 1e-3
+    td = sum(e[1].elapsed_time(e[2]) for e in ev) / n * 1e-3
+    b_app = b_dec = 0
+    for s in range(n_steps):
+        lb = np.full(B, ctx + s, np.int64)
+        b_app += _append_bytes(lb, hkv, R)
+        b_dec += _decode_bytes(lb + 1, hkv, hq, R)
+    b_app, b_dec = b_app / n_steps, b_dec / n_steps
+    step = elapsed / n
+    return {"workload": f"{B} seqs x {ctx}+ tokens, {hq} q / {hkv} kv heads, {FORMAT}, {n_steps} append + decode "
+                        f"steps on each of {n_copies} cache copies (one tail fill per sequence per copy)",
+            "us_per_step": step * 1e6, "tokens_per_s": B / step, "step_GBps": (b_app + b_dec) / step / 1e9,
+            "step_frac_hbm": (b_app + b_dec) / step / 1e9 / HBM_PEAK_GBPS,
+            "decode_us": td * 1e6, "decode_bytes": b_dec, "decode_GBps": b_dec / td / 1e9,
+            "decode_frac_hbm": b_dec / td / 1e9 / HBM_PEAK_GBPS, "decode_tokens_per_s": B / td,
+            "append_us": ta * 1e6, "append_bytes": b_app}
+
+
+def ragged_mixed_steps(kv, synth, dev, steps):
+    """64 sequences with lengths uniform in [1024, 32768], 32 query / 4 kv heads, each sequence k4v2 or
+    k8v8 (one pool and one append + decode call per format).  Each step appends one token to every
+    sequence (tiles that fill are quantised inline) and decodes; the step reads ~0.9 GB, well past the
+    Infinity Cache.  Full pages are quantised beforehand from fp16 K/V ~ N(0, 1.5^2) drawn on the device
+    (the kernels' time does not depend on the values)."""
+    import numpy as np
+    import torch
+    w = synth.WORKLOADS["ragged_mixed_64seq"]
+    B, hq, hkv = w["batch"], w["n_q_heads"], w["n_kv_heads"]
+    lens0 = synth.gen_lengths(w["seed"], B, w["ctx_lo"], w["ctx_hi"]).astype(np.int64)
+    fmts = synth.gen_formats(w["seed"], B)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w["seed"])
+    q_all = synth.gen_q(w["seed"], B, hq)
+    rng = np.random.default_rng(w["seed"] + 7)
+    sm = 1.0 / math.sqrt(128)
+    n_steps = max(1, min(steps, 100))
+    pools = []
+    for fi, name in enumerate(("kvarn_k4v2_g128", "kvarn_k8v8_g128")):
+        idx = np.nonzero(fmts == fi)[0]
+        if len(idx) == 0:
+            continue
+        fmt = kv.format_parse(name)
+        R = kv.record_bytes(fmt)
+        stride = hkv * R
+        lens = lens0[idx]
+        full = lens // 128
+        maxp = int(full.max()) + 2
+        n = len(idx)
+        pt_h = synth.gen_page_perm(w["seed"] + fi, n * maxp).reshape(n, maxp)
+        cache = torch.zeros(n * maxp * stride, dtype=torch.uint8, device=dev)
+        dst = np.concatenate([pt_h[i, :full[i]] for i in range(n)]).astype(np.int32)
+        for c0 in range(0, len(dst), 2048):
+            m = min(2048, len(dst) - c0)
+            kt = (torch.randn(m, 128, hkv, 128, generator=gen, device=dev) * 1.5).half()
+            vt = (torch.randn(m, 128, hkv, 128, generator=gen, device=dev) * 1.5).half()
+            kv.quantize_tiles(fmt, kt, vt, torch.from_numpy(dst[c0:c0 + m]).to(dev), cache, stride)
+        tk = (torch.randn(n, hkv, 128, 128, generator=gen, device=dev) * 1.5).half()
+        tv = (torch.randn(n, hkv, 128, 128, generator=gen, device=dev) * 1.5).half()
+        knew = torch.from_numpy((rng.standard_normal((n_steps, n, hkv, 128)) * 1.5).astype(np.float16)).to(dev)
+        vnew = torch.from_numpy((rng.standard_normal((n_steps, n, hkv, 128)) * 1.5).astype(np.float16)).to(dev)
+        pools.append(dict(name=name, fmt=fmt, R=R, stride=stride, lens0=lens.copy(), cache=cache, tk=tk, tv=tv,
+                          pt=torch.from_numpy(np.ascontiguousarray(pt_h)).to(dev), knew=knew, vnew=vnew,
+                          lens=torch.from_numpy(lens.astype(np.int32)).to(dev),
+                          q=torch.from_numpy(q_all[idx]).to(dev),
+                          out=torch.empty(n, hq, 128, dtype=torch.float16, device=dev),
+                          ws=kv.decode_workspace(fmt, n, hq, hkv, maxp, dev)))
+
+    for p in pools:
+        p["apps"] = [kv.prepare_append_token(p["fmt"], p["knew"][s], p["vnew"][s], p["lens"], p["tk"], p["tv"],
+                                             p["pt"], p["cache"], p["stride"]) for s in range(n_steps)]
+        p["dec"] = kv.prepare_decode_attention(p["fmt"], p["q"], p["cache"], p["stride"], p["pt"], p["lens"], p["tk"],
+                                               p["tv"], sm, p["out"], p["ws"], hkv)
+
+    def run(nst):
+        for s in range(nst):
+            for p in pools:
+                p["apps"][s]()
+                p["dec"]()
+
+    run(1)                                         # warm-up, then back to the starting lengths
+    torch.cuda.synchronize(dev)
+    for p in pools:
+        p["lens"].copy_(torch.from_numpy(p["lens0"].astype(np.int32)))
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(n_steps)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    step = e0.elapsed_time(e1) * 1e-3 / n_steps
+    total = fills = 0
+    for p in pools:
+        assert np.array_equal(p["lens"].cpu().numpy(), p["lens0"] + n_steps)
+        for s in range(n_steps):
+            lb = p["lens0"] + s
+            total += _append_bytes(lb, hkv, p["R"]) + _decode_bytes(lb + 1, hkv, hq, p["R"])
+            fills += int(((lb + 1) % 128 == 0).sum())
+    per_step = total / n_steps
+    return {"workload": (f"{B} seqs, lengths U[{w['ctx_lo']}, {w['ctx_hi']}] (seeded), {hq} q / {hkv} kv heads, "
+                         f"formats " + " / ".join(f"{p['name']} x {len(p['lens0'])}" for p in pools)
+                         + f", {n_steps} append + decode steps"),
+            "us_per_step": step * 1e6, "bytes_per_step": per_step, "GBps": per_step / step / 1e9,
+            "frac_hbm": per_step / step / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": B / step,
+            "tile_fills": fills}
 
 
 def main():
@@ -410,6 +611,14 @@ def main():
     elapsed = time.perf_counter() - t0
     assert torch.isfinite(out2.float()).all().item()
 
+    # the "achievable" line: a plain device-to-device copy that moves as many bytes (read + write) as
+    # one bulk quantise, two copies alternated like the step's inputs (outside the timed step)
+    n_copy = quant_bytes // 2 // 256 * 256
+    csrc = [torch.empty(n_copy, dtype=torch.uint8, device=dev).fill_(1) for _ in range(2)]
+    cdst = [torch.empty_like(s) for s in csrc]
+    t_copy = _events_time(lambda i: cdst[i % 2].copy_(csrc[i % 2]), 20, 3)
+    del csrc, cdst
+
     tq = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev) * 1e-3
     ta = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev) * 1e-3
     td = sum(e[2].elapsed_time(e[3]) for e in ev) / len(ev) * 1e-3
@@ -428,6 +637,9 @@ def main():
         "decode_attention": {"GBps": dec_b / td / 1e9, "frac_hbm": dec_b / td / 1e9 / HBM_PEAK_GBPS,
                              "us": td * 1e6, "bytes": dec_b, "tokens_per_s": D_B / td,
                              "note": "decode kernel (split-K partials merged by the last workgroup); one layer call, 1 token per sequence"},
+        "device_copy": {"us": t_copy * 1e6, "bytes": 2 * n_copy, "GBps": 2 * n_copy / t_copy / 1e9,
+                        "frac_hbm": 2 * n_copy / t_copy / 1e9 / HBM_PEAK_GBPS,
+                        "note": "plain device copy of the quantise's byte count (read + write): the achievable line"},
     }
     dom = "quantize_tiles" if tq >= td else "decode_attention"
     dk = kernels[dom]

@@ -8,7 +8,9 @@ on first use; there is no CPU fallback.
 Functions mirror include/libkvarn.h:
     format_parse, record_bytes, decode_workspace_bytes,
     quantize_tiles, append_token, decode_attention, prefill_attention
-plus decode_workspace (a zero-filled workspace tensor for decode_attention).
+plus decode_workspace (a zero-filled workspace tensor for decode_attention) and
+prepare_append_token / prepare_decode_attention (the same calls with their arguments marshalled
+once, for serving loops whose kernels take a few microseconds).
 """
 from __future__ import annotations
 
@@ -160,10 +162,7 @@ def quantize_tiles(fmt: Format, k, v, dst_pages, cache, page_stride_bytes: int, 
     _check(st, "kvarn_quantize_tiles")
 
 
-def append_token(fmt: Format, k_new, v_new, seq_lens, tail_k, tail_v, page_table, cache, page_stride_bytes: int,
-                 stream=None):
-    """k_new, v_new: fp16 [B, Hkv, 128]; seq_lens int32 [B] (incremented); tails fp16 [B, Hkv, 128, 128];
-    page_table int32 [B, max_pages]."""
+def _append_args(fmt, k_new, v_new, seq_lens, tail_k, tail_v, page_table, cache, page_stride_bytes, stream):
     import torch
     _need(k_new, "k_new", torch.float16, 3)
     _need(v_new, "v_new", torch.float16, 3)
@@ -176,17 +175,20 @@ def append_token(fmt: Format, k_new, v_new, seq_lens, tail_k, tail_v, page_table
     if (v_new.shape != k_new.shape or tuple(tail_k.shape) != (B, hkv, 128, 128) or tail_v.shape != tail_k.shape
             or seq_lens.shape[0] != B or page_table.shape[0] != B):
         raise ValueError("inconsistent shapes for append_token")
-    st = lib().kvarn_append_token(ctypes.byref(fmt), B, hkv, _ptr(k_new), _ptr(v_new), _ptr(seq_lens), _ptr(tail_k),
-                                  _ptr(tail_v), _ptr(page_table), page_table.shape[1], _ptr(cache),
-                                  page_stride_bytes, _stream(stream))
-    _check(st, "kvarn_append_token")
+    return (ctypes.byref(fmt), B, hkv, _ptr(k_new), _ptr(v_new), _ptr(seq_lens), _ptr(tail_k), _ptr(tail_v),
+            _ptr(page_table), page_table.shape[1], _ptr(cache), page_stride_bytes, _stream(stream))
 
 
-def decode_attention(fmt: Format, q, cache, page_stride_bytes: int, page_table, seq_lens, tail_k, tail_v,
-                     sm_scale: float, out, workspace, num_kv_heads: int, stream=None):
-    """q, out: fp16 [B, Hq, 128]; page_table int32 [B, max_pages]; seq_lens int32 [B];
-    tails fp16 [B, Hkv, 128, 128]; workspace: device tensor of >= decode_workspace_bytes bytes whose
-    arrival counters are zero (zero-filled once, e.g. by decode_workspace; each call leaves them zero)."""
+def append_token(fmt: Format, k_new, v_new, seq_lens, tail_k, tail_v, page_table, cache, page_stride_bytes: int,
+                 stream=None):
+    """k_new, v_new: fp16 [B, Hkv, 128]; seq_lens int32 [B] (incremented); tails fp16 [B, Hkv, 128, 128];
+    page_table int32 [B, max_pages]."""
+    args = _append_args(fmt, k_new, v_new, seq_lens, tail_k, tail_v, page_table, cache, page_stride_bytes, stream)
+    _check(lib().kvarn_append_token(*args), "kvarn_append_token")
+
+
+def _decode_args(fmt, q, cache, page_stride_bytes, page_table, seq_lens, tail_k, tail_v, sm_scale, out, workspace,
+                 num_kv_heads, stream):
     import torch
     _need(q, "q", torch.float16, 3)
     _need(out, "out", torch.float16, 3)
@@ -203,11 +205,52 @@ def decode_attention(fmt: Format, q, cache, page_stride_bytes: int, page_table, 
     if tuple(tail_k.shape) != (B, num_kv_heads, 128, 128) or tail_v.shape != tail_k.shape:
         raise ValueError(f"tails must be [B, Hkv, 128, 128], got {tuple(tail_k.shape)}")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().kvarn_decode_attention(ctypes.byref(fmt), B, hq, num_kv_heads, _ptr(q), _ptr(cache),
-                                      page_stride_bytes, _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
-                                      _ptr(tail_k), _ptr(tail_v), float(sm_scale), _ptr(out), _ptr(workspace),
-                                      ws_bytes, _stream(stream))
-    _check(st, "kvarn_decode_attention")
+    return (ctypes.byref(fmt), B, hq, num_kv_heads, _ptr(q), _ptr(cache), page_stride_bytes, _ptr(page_table),
+            page_table.shape[1], _ptr(seq_lens), _ptr(tail_k), _ptr(tail_v), float(sm_scale), _ptr(out),
+            _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def decode_attention(fmt: Format, q, cache, page_stride_bytes: int, page_table, seq_lens, tail_k, tail_v,
+                     sm_scale: float, out, workspace, num_kv_heads: int, stream=None):
+    """q, out: fp16 [B, Hq, 128]; page_table int32 [B, max_pages]; seq_lens int32 [B];
+    tails fp16 [B, Hkv, 128, 128]; workspace: device tensor of >= decode_workspace_bytes bytes whose
+    arrival counters are zero (zero-filled once, e.g. by decode_workspace; each call leaves them zero)."""
+    args = _decode_args(fmt, q, cache, page_stride_bytes, page_table, seq_lens, tail_k, tail_v, sm_scale, out,
+                        workspace, num_kv_heads, stream)
+    _check(lib().kvarn_decode_attention(*args), "kvarn_decode_attention")
+
+
+class PreparedCall:
+    """One C-ABI call whose arguments were checked and marshalled once (the tensors it points to are
+    held here).  Calling it only re-issues the call on the stream it was prepared for, for loops whose
+    GPU work per call is a few microseconds and whose host time would otherwise dominate."""
+
+    def __init__(self, fn, args, what, keep):
+        self._fn, self._args, self._what, self._keep = fn, args, what, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != KVARN_OK:
+            raise KvarnError(st, self._what)
+
+
+def prepare_append_token(fmt: Format, k_new, v_new, seq_lens, tail_k, tail_v, page_table, cache,
+                         page_stride_bytes: int, stream=None) -> PreparedCall:
+    """append_token with the same arguments, checked and marshalled once: returns a callable that
+    issues it on the stream current now (or `stream`)."""
+    args = _append_args(fmt, k_new, v_new, seq_lens, tail_k, tail_v, page_table, cache, page_stride_bytes, stream)
+    return PreparedCall(lib().kvarn_append_token, args, "kvarn_append_token",
+                        (fmt, k_new, v_new, seq_lens, tail_k, tail_v, page_table, cache))
+
+
+def prepare_decode_attention(fmt: Format, q, cache, page_stride_bytes: int, page_table, seq_lens, tail_k, tail_v,
+                             sm_scale: float, out, workspace, num_kv_heads: int, stream=None) -> PreparedCall:
+    """decode_attention with the same arguments, checked and marshalled once: returns a callable
+    that issues it on the stream current now (or `stream`)."""
+    args = _decode_args(fmt, q, cache, page_stride_bytes, page_table, seq_lens, tail_k, tail_v, sm_scale, out,
+                        workspace, num_kv_heads, stream)
+    return PreparedCall(lib().kvarn_decode_attention, args, "kvarn_decode_attention",
+                        (fmt, q, cache, page_table, seq_lens, tail_k, tail_v, out, workspace))
 
 
 def prefill_attention(fmt: Format, q, q_lens, cache, page_stride_bytes: int, page_table, seq_lens, tail_k, tail_v,

@@ -153,10 +153,12 @@ __device__ __forceinline__ void tail_heads(const _Float16* __restrict__ q0, int 
 // One wave; lane l owns output channels 2l and 2l + 1.  With M the largest running maximum (log2
 // units) over the splits and f_k = exp2(M_k - M):
 //   L = sum_k f_k L_k,  rot = sum_k f_k rot_k (rotated domain),  raw = sum_k f_k raw_k (the fp16 tail,
-//   raw domain, only in splits that own tail tokens),  out = (Hn rot + raw) / L,
-// all zero for an empty sequence.  part: the n_splits partials of this head.
-__device__ __forceinline__ void combine_head(const float* __restrict__ part, int n_splits, _Float16* __restrict__ o,
-                                             int lane) {
+//   raw domain, only in the first n_tail splits, which own tail tokens),  out = (Hn rot + raw) / L,
+// all zero for an empty sequence.  part: the n_splits partials of this head.  The split loops are
+// unrolled deeply and their loads do not depend on earlier loads, so the rows of many splits are in
+// flight at once (a long sequence with few (sequence, kv head) pairs has ~100 splits).
+__device__ __forceinline__ void combine_head(const float* __restrict__ part, int n_splits, int n_tail,
+                                             _Float16* __restrict__ o, int lane) {
   float M = -INFINITY;
   for (int k = lane; k < n_splits; k += 64) M = fmaxf(M, load_agent(part + k * kPartialFloats));
 #pragma unroll
@@ -164,22 +166,30 @@ __device__ __forceinline__ void combine_head(const float* __restrict__ part, int
 
   float L = 0.f, r[2] = {0.f, 0.f}, w[2] = {0.f, 0.f};
   if (M != -INFINITY) {
-    // an empty split holds (-inf, 0, 0...): its factor exp2(-inf) is 0
-#pragma unroll 4
-    for (int k = 0; k < n_splits; ++k) {
+    // an empty split holds (-inf, 0, 0...): its factor exp2(-inf) is 0.  The first n_tail splits
+    // own tail tokens (a split's share is at least one token) and carry raw-domain sums too.
+#pragma unroll 8
+    for (int k = 0; k < n_tail; ++k) {
       const float* pk = part + k * kPartialFloats;
       const float2 ml = load_agent2(pk);
-      const float2 fl = load_agent2(pk + 2);
+      const float2 a = load_agent2(pk + 4 + 2 * lane);
+      const float2 b = load_agent2(pk + 4 + kCh + 2 * lane);
       const float f = __builtin_amdgcn_exp2f(ml.x - M);
       L = fmaf(ml.y, f, L);
-      const float2 a = load_agent2(pk + 4 + 2 * lane);
       r[0] = fmaf(a.x, f, r[0]);
       r[1] = fmaf(a.y, f, r[1]);
-      if (fl.x != 0.f) {
-        const float2 b = load_agent2(pk + 4 + kCh + 2 * lane);
-        w[0] = fmaf(b.x, f, w[0]);
-        w[1] = fmaf(b.y, f, w[1]);
-      }
+      w[0] = fmaf(b.x, f, w[0]);
+      w[1] = fmaf(b.y, f, w[1]);
+    }
+#pragma unroll 32
+    for (int k = n_tail; k < n_splits; ++k) {
+      const float* pk = part + k * kPartialFloats;
+      const float2 ml = load_agent2(pk);
+      const float2 a = load_agent2(pk + 4 + 2 * lane);
+      const float f = __builtin_amdgcn_exp2f(ml.x - M);
+      L = fmaf(ml.y, f, L);
+      r[0] = fmaf(a.x, f, r[0]);
+      r[1] = fmaf(a.y, f, r[1]);
     }
   }
   // Hn over the rotated-domain sum: one stage in registers, six across lanes
@@ -725,9 +735,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   __syncthreads();
   if (!last_wg) return;
   if (tid == 0) __hip_atomic_store(counters + sh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // splits that own tail tokens: the first ceil(nt / tps) (split sp owns tokens sp*tps .. sp*tps+tps-1)
+  const int n_tail = tps > 0 ? (nt + tps - 1) / tps : 0;
   for (int g = wave; g < G; g += 4) {
     const int64_t sq = static_cast<int64_t>(s) * num_q_heads + h * G + g;
-    combine_head(ws + sq * n_splits * kPartialFloats, n_splits, out + sq * kCh, lane);
+    combine_head(ws + sq * n_splits * kPartialFloats, n_splits, n_tail, out + sq * kCh, lane);
   }
 }
 

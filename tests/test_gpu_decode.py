@@ -223,3 +223,47 @@ def test_workspace_counters_return_to_zero():
     assert np.array_equal(other.view(np.uint16), b.run_gpu().view(np.uint16))
     _compare(first, a.run_oracle(), a.lens)
     _compare(other, b.run_oracle(), b.lens)
+
+
+def test_merge_of_many_splits_with_a_full_tail():
+    """One long sequence on one kv head: ~130 split-K workgroups, and a 127-token tail shared one
+    token per split, so the merge reads the raw-domain rows of more than 64 splits (two header
+    chunks); against the oracle, plus an L = 1 sequence in the same call."""
+    st = Setup("kvarn_k4v2_g128", [253 * 128 + 127, 1], hkv=1, hq=8, seed=33)
+    out = st.run_gpu()
+    _compare(out, st.run_oracle(), st.lens)
+
+
+def test_prepared_calls_match_plain_calls():
+    """prepare_append_token / prepare_decode_attention issue the same C-ABI calls as append_token /
+    decode_attention: bit-identical tails, lengths, cache bytes and outputs."""
+    st = Setup("kvarn_k4v2_g128", [3 * 128 + 126, 700, 130], hkv=2, hq=8, seed=34, max_pages=6)
+    rng = np.random.default_rng(35)
+    k_new = torch.from_numpy((rng.standard_normal((st.B, st.hkv, 128)) * 1.5).astype(np.float16)).to(DEV)
+    v_new = torch.from_numpy((rng.standard_normal((st.B, st.hkv, 128)) * 1.5).astype(np.float16)).to(DEV)
+    pt = torch.from_numpy(np.ascontiguousarray(st.pt)).to(DEV)
+    q = torch.from_numpy(st.q).to(DEV)
+    states = []
+    for prepared in (False, True):
+        cache = st.cache.clone()
+        lens = torch.from_numpy(st.lens.copy()).to(DEV)
+        tk = torch.from_numpy(st.tail_k.copy()).to(DEV)
+        tv = torch.from_numpy(st.tail_v.copy()).to(DEV)
+        ws = kv.decode_workspace(st.fmt, st.B, st.hq, st.hkv, pt.shape[1], DEV)
+        out = torch.empty(st.B, st.hq, 128, dtype=torch.float16, device=DEV)
+        app = (st.fmt, k_new, v_new, lens, tk, tv, pt, cache, st.stride)
+        dec = (st.fmt, q, cache, st.stride, pt, lens, tk, tv, st.sm, out, ws, st.hkv)
+        if prepared:
+            a, d = kv.prepare_append_token(*app), kv.prepare_decode_attention(*dec)
+            for _ in range(3):
+                a()
+                d()
+        else:
+            for _ in range(3):
+                kv.append_token(*app)
+                kv.decode_attention(*dec)
+        torch.cuda.synchronize()
+        states.append([t.cpu().numpy() for t in (cache, lens, tk, tv, out)])
+    assert states[1][1].tolist() == (st.lens + 3).tolist()
+    for x, y in zip(*states):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
