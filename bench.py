@@ -130,6 +130,17 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
     print(json.dumps(out))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(k1, v1, seconds):
     """The oracle, as it stands, on a bounded sample of the same workload: whole sequences of the
     bulk-quantise batch, then decode steps over oracle-quantised sequences of the decode shape."""
@@ -168,7 +179,22 @@ def cpu_baseline(k1, v1, seconds):
         d_bytes += 128 * Q_HKV * R + 2 * D_HQ * 256
         d_calls += 1
     rate = (q_bytes + d_bytes) / (q_time + d_time) / 1e9
-    return {"value": rate, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    # single-thread runs: the single-tile workload (1 kv head, 128 tokens, seed 0) and a 64-tile subset
+    # of the bulk batch (64 tiles x 4 kv heads)
+    k0, v0 = synth.gen_kv(0, 128, 1)
+    c0 = np.zeros(R, np.uint8)
+    t0 = time.perf_counter()
+    oracle.quantize_tiles(4, 2, 8, synth.tiles_view(k0).view(np.uint16), synth.tiles_view(v0).view(np.uint16),
+                          np.zeros(1, np.int32), c0, R, nthreads=1)
+    t_single = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.quantize_tiles(4, 2, 8, np.ascontiguousarray(kt[:64]).view(np.uint16),
+                          np.ascontiguousarray(vt[:64]).view(np.uint16), pages[:64], cache, Q_HKV * R, nthreads=1)
+    t_sub = time.perf_counter() - t0
+    sub_bytes = 64 * Q_HKV * (2 * 128 * 128 * 2 + R)
+    return {"value": rate, "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": _cpu_model(),
+            "single_thread": {"single_tile_quantize_ms": t_single * 1e3,
+                              "bulk_64_tiles_quantize_s": t_sub, "bulk_64_tiles_quantize_GBps": sub_bytes / t_sub / 1e9},
             "sample": (f"{q_seqs} sequence(s) of 128 tiles x 4 kv heads quantised ({q_bytes / 1e6:.1f} MB, "
                        f"{q_time:.1f} s) + {d_calls} decode call(s) of 1 sequence x 16384 tokens x 32 query "
                        f"heads ({d_bytes / 1e6:.1f} MB, {d_time:.1f} s); fp64 oracle, {threads} threads"),
