@@ -112,7 +112,11 @@ kvarn_status kvarn_quantize_tiles(const kvarn_format* f, int32_t num_tiles, int3
  *   seq_lens      (device) int32 [num_seqs], read then incremented
  *   tail_k/tail_v (device) fp16 [num_seqs][num_kv_heads][128][head_dim]
  *   page_table    (device) int32 [num_seqs][max_pages_per_seq]
- * The page for a filling tile must be allocated in page_table before the call. */
+ * The page for a filling tile must be allocated in page_table before the call.
+ * One launch reads and advances the lengths: while it runs, seq_lens[s] holds the number of kv
+ * heads already appended in its bits 24 and up, so lengths must stay below 2^24 tokens, at most
+ * 64 kv heads are supported (more return KVARN_E_UNSUPPORTED), and nothing else may read seq_lens
+ * until the call's work has completed (calls on one stream are ordered). */
 kvarn_status kvarn_append_token(const kvarn_format* f, int32_t num_seqs, int32_t num_kv_heads,
                                 const void* k_new, const void* v_new, int32_t* seq_lens, void* tail_k,
                                 void* tail_v, const int32_t* page_table, int32_t max_pages_per_seq,

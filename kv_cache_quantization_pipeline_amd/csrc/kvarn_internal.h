@@ -34,6 +34,11 @@ DecodePlan plan_decode(int kb, int vb, int ng, int num_seqs, int num_kv_heads, i
 // tail accumulators (written only with the flag set).  The counters must be zero when a launch
 // starts; every launch leaves them zero.
 constexpr int kPartialFloats = 260;
+
+// The append kernel counts the arrivals of a sequence's kv-head workgroups in the bits of
+// seq_lens[s] from this one up, so lengths stay below 2^24 tokens and kv heads at most 64.
+constexpr int kArrivalShift = 24;
+constexpr int kMaxAppendKvHeads = 64;
 inline size_t decode_counter_bytes(int num_seqs, int num_kv_heads) {
   return (static_cast<size_t>(num_seqs) * num_kv_heads * sizeof(int32_t) + 255) / 256 * 256;
 }

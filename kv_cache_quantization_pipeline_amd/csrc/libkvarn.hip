@@ -109,6 +109,7 @@ kvarn_status kvarn_append_token(const kvarn_format* f, int32_t num_seqs, int32_t
   const kvarn_status st = check_format(f);
   if (st != KVARN_OK) return st;
   if (num_seqs < 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0) return KVARN_E_INVALID_ARG;
+  if (num_kv_heads > kvarn::kMaxAppendKvHeads) return KVARN_E_UNSUPPORTED;
   if (num_seqs == 0) return KVARN_OK;
   if (k_new == nullptr || v_new == nullptr || seq_lens == nullptr || tail_k == nullptr || tail_v == nullptr ||
       page_table == nullptr || cache == nullptr)

@@ -573,10 +573,15 @@ __global__ __launch_bounds__(128, 2) void quantize_tiles_kernel(const _Float16* 
 // Token append: one workgroup per (sequence, kv head).  Writes the new token into
 // the fp16 tail at len % 128 and, when that fills the tile, quantises the tail
 // (token 127 read from the new token itself) into page_table[s][len / 128].
+// The length is read and advanced in the same launch: each workgroup of sequence s adds
+// 1 << kArrivalShift to seq_lens[s] and takes len from the low bits of the old value, and the one
+// that counts the last arrival takes the count back out and adds the new token.  Every workgroup
+// thus reads len before any change to the low bits (len < 2^kArrivalShift; at most 64 kv heads,
+// so the word never overflows).
 template <int KB, int VB, int NG>
 __global__ __launch_bounds__(256, 2) void append_kernel(const _Float16* __restrict__ k_new,
                                                         const _Float16* __restrict__ v_new,
-                                                        const int32_t* __restrict__ seq_lens,
+                                                        int32_t* __restrict__ seq_lens,
                                                         _Float16* __restrict__ tail_k, _Float16* __restrict__ tail_v,
                                                         const int32_t* __restrict__ page_table, int max_pages,
                                                         uint8_t* __restrict__ cache, int64_t page_stride,
@@ -586,7 +591,14 @@ __global__ __launch_bounds__(256, 2) void append_kernel(const _Float16* __restri
   const int sh = blockIdx.x;
   const int s = sh / num_kv_heads;
   const int h = sh - s * num_kv_heads;
-  const int len = seq_lens[s];
+  __shared__ int len_sh;
+  if (threadIdx.x == 0) {
+    const int old = atomicAdd(seq_lens + s, 1 << kArrivalShift);
+    len_sh = old & ((1 << kArrivalShift) - 1);
+    if ((old >> kArrivalShift) == num_kv_heads - 1) atomicAdd(seq_lens + s, 1 - (num_kv_heads << kArrivalShift));
+  }
+  __syncthreads();
+  const int len = len_sh;
   const int slot = len & (kTok - 1);
   const int64_t tail_base = static_cast<int64_t>(sh) * kTok * kCh;
   const int tid = threadIdx.x;
@@ -605,11 +617,6 @@ __global__ __launch_bounds__(256, 2) void append_kernel(const _Float16* __restri
         cache + static_cast<int64_t>(page) * page_stride + static_cast<int64_t>(h) * record_bytes(KB, VB, NG);
     quantize_tile_half<KB, VB, NG>(x, kCh, last, rec, iters, is_v, xch, wlds);
   }
-}
-
-__global__ void seq_len_increment_kernel(int32_t* __restrict__ seq_lens, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) seq_lens[i] += 1;
 }
 
 // (kb, vb, groups per token) -> the kernel instantiation for that format
@@ -648,9 +655,7 @@ hipError_t launch_append(const _Float16* k_new, const _Float16* v_new, int32_t* 
   }
   KVARN_FOR_EACH_FORMAT(KVARN_A)
 #undef KVARN_A
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seq_len_increment_kernel, dim3((num_seqs + 255) / 256), dim3(256), 0, stream, seq_lens, num_seqs);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace kvarn

@@ -104,6 +104,9 @@ def test_calls_reject_bad_arguments_before_launch():
     assert L.kvarn_append_token(fp, 2, 2, dummy, dummy, dummy, dummy, dummy, dummy, 0, dummy, 2 * R, None) \
         == kv.KVARN_E_INVALID_ARG
     assert L.kvarn_append_token(fp, 0, 2, None, None, None, None, None, None, 4, None, 2 * R, None) == kv.KVARN_OK
+    # the lengths word counts kv-head arrivals in its bits 24 and up: at most 64 kv heads
+    assert L.kvarn_append_token(fp, 2, 65, dummy, dummy, dummy, dummy, dummy, dummy, 4, dummy, 65 * R, None) \
+        == kv.KVARN_E_UNSUPPORTED
     # decode: GQA ratio, workspace size / alignment, nulls
     ws_need = kv.decode_workspace_bytes(f, 2, 16, 2, 4)
     args = dict(q=dummy, cache=dummy, pt=dummy, sl=dummy, tk=dummy, tv=dummy, out=dummy, ws=dummy)
