@@ -258,3 +258,49 @@ def test_append_ragged_against_oracle():
                 else:
                     assert np.all(gc[off:off + R] == 0x5A), (s, p, h)
     assert_code_rate(n_bad, 3 * hkv * 2 * 128 * 128)
+
+
+def test_append_at_most_kv_heads_counts_arrivals():
+    """64 kv heads (the most the append supports: their arrivals are counted in the length word's
+    high bits) over 3 sequences, one of which fills a tile: lengths advance by exactly one, every
+    tail slot holds its token, and the filled records equal the bulk quantiser's on the same tokens."""
+    fmt = _fmt("kvarn_k4v2_g128")
+    B, hkv = 3, 64
+    R = kv.record_bytes(fmt)
+    stride = hkv * R
+    rng = np.random.default_rng(16)
+    lens0 = np.array([127, 1000, 3], np.int32)
+    tails_k = rng.standard_normal((B, hkv, 128, 128)).astype(np.float16)
+    tails_v = rng.standard_normal((B, hkv, 128, 128)).astype(np.float16)
+    k_new = rng.standard_normal((B, hkv, 128)).astype(np.float16)
+    v_new = rng.standard_normal((B, hkv, 128)).astype(np.float16)
+    pt = np.array([[1, 0], [2, 3], [4, 5]], np.int32)
+    cache = torch.zeros(6 * stride, dtype=torch.uint8, device=DEV)
+    lens = torch.from_numpy(lens0.copy()).to(DEV)
+    tk = torch.from_numpy(tails_k.copy()).to(DEV)
+    tv = torch.from_numpy(tails_v.copy()).to(DEV)
+    for rep in range(2):
+        kv.append_token(fmt, torch.from_numpy(k_new).to(DEV), torch.from_numpy(v_new).to(DEV), lens, tk, tv,
+                        torch.from_numpy(pt).to(DEV), cache, stride)
+        torch.cuda.synchronize()
+        assert lens.cpu().tolist() == (lens0 + rep + 1).tolist()
+    exp_k, exp_v = tails_k.copy(), tails_v.copy()
+    for rep in range(2):
+        for s in range(B):
+            exp_k[s, :, (lens0[s] + rep) % 128] = k_new[s]
+            exp_v[s, :, (lens0[s] + rep) % 128] = v_new[s]
+    assert np.array_equal(tk.cpu().numpy().view(np.uint16), exp_k.view(np.uint16))
+    assert np.array_equal(tv.cpu().numpy().view(np.uint16), exp_v.view(np.uint16))
+    # sequence 0 filled its tile on the first append (token 127 = k_new) into page pt[0][0] = 1
+    fk = exp_k[0].copy()
+    fv = exp_v[0].copy()
+    fk[:, 127] = k_new[0]
+    fv[:, 127] = v_new[0]
+    fk[:, 0] = tails_k[0][:, 0]
+    fv[:, 0] = tails_v[0][:, 0]
+    bulk = torch.zeros_like(cache)
+    kv.quantize_tiles(fmt, torch.from_numpy(np.ascontiguousarray(fk.transpose(1, 0, 2))[None]).to(DEV),
+                      torch.from_numpy(np.ascontiguousarray(fv.transpose(1, 0, 2))[None]).to(DEV),
+                      torch.tensor([1], dtype=torch.int32, device=DEV), bulk, stride)
+    torch.cuda.synchronize()
+    assert torch.equal(cache, bulk)
