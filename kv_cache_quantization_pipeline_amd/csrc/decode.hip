@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
                                                         int max_pages, const int32_t* __restrict__ seq_lens,
                                                         int num_q_heads, int num_kv_heads, float qscale,
                                                         float* __restrict__ ws, int* __restrict__ counters,
-                                                        int n_splits,
+                                                        int n_splits, int tail_splits,
                                                         const _Float16* __restrict__ tail_k,
                                                         const _Float16* __restrict__ tail_v, float sm_log2e,
                                                         _Float16* __restrict__ out) {
@@ -316,12 +316,16 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[nb][i] = 0.f;
 
-  // this sequence's groups split evenly over the n_splits workgroups of the pair (the grid is sized
-  // for the longest sequence), then over the 4 waves of each
-  const int gps = (n_groups + n_splits - 1) / n_splits;
+  // this sequence's groups split evenly over the page splits of the pair (all n_splits workgroups,
+  // or those after the tail_splits tail-only ones; the grid is sized for the longest sequence), then
+  // over the 4 waves of each
+  const int nps = n_splits - tail_splits;
+  const int gps = (n_groups + nps - 1) / nps;
   const int gpw = (gps + 3) / 4;
-  const int s_end = min(sp * gps + gps, n_groups);
-  const int g_begin = sp * gps + wave * gpw;
+  // a tail-only split (sp < tail_splits) takes the empty group range [n_groups, n_groups)
+  const int base = sp >= tail_splits ? (sp - tail_splits) * gps : n_groups;
+  const int s_end = min(base + gps, n_groups);
+  const int g_begin = base + wave * gpw;
   const int g_end = min(g_begin + gpw, s_end);
   const int64_t pt_row = static_cast<int64_t>(s) * max_pages;
   const int64_t head_off = static_cast<int64_t>(h) * R;
@@ -661,7 +665,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const _Float16* __restri
   constexpr int HW = (G + 3) / 4;
   __shared__ float tail_ml[2][G];
   const int nt = len & (kTok - 1);
-  const int tps = (nt + n_splits - 1) / n_splits;
+  // the tail owners: the first tail_splits splits, or all of them (then a split's share is small)
+  const int owners = tail_splits > 0 ? tail_splits : n_splits;
+  const int tps = (nt + owners - 1) / owners;
   const int t0 = min(nt, sp * tps), t1 = min(nt, t0 + tps);
   const bool has_tail = t1 > t0;
   if (has_tail && wave < G) {
@@ -752,7 +758,7 @@ static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64
   const float qscale = sm_scale * kLog2e * 0.08838834764831845f;
   hipLaunchKernelGGL((decode_kernel<KB, VB, G, NG>), dim3(num_seqs * num_kv_heads, plan.n_splits), dim3(256), 0, stream,
                      q, cache, page_stride, page_table, max_pages, seq_lens, num_q_heads, num_kv_heads, qscale,
-                     workspace, counters, plan.n_splits, tail_k, tail_v, sm_scale * kLog2e, out);
+                     workspace, counters, plan.n_splits, plan.tail_splits, tail_k, tail_v, sm_scale * kLog2e, out);
   return hipGetLastError();
 }
 
@@ -802,12 +808,24 @@ DecodePlan plan_decode(int kb, int vb, int ng, int num_seqs, int num_kv_heads, i
   const int target_wgs = (kb == 8 || vb == 8) ? 256 : 512;
   int splits0 = units > 0 ? (target_wgs + units - 1) / units : 1;
   if (splits0 < 1) splits0 = 1;
-  const int gps = groups_max > 0 ? (groups_max + splits0 - 1) / splits0 : 1;
+  // groups per split: a multiple of 4, so that each of the 4 waves of a workgroup gets the same count
+  int gps = groups_max > 0 ? (groups_max + splits0 - 1) / splits0 : 1;
+  gps = (gps + 3) / 4 * 4;
   p.groups_per_split = gps;
-  p.n_splits = groups_max > 0 ? (groups_max + gps - 1) / gps : 1;
-  // the fp16 tail (up to 127 tokens) is shared out among the splits: at least 8 of them where the
-  // grid has room, so that a split's share is one 16-token chunk
-  p.n_splits = std::max(p.n_splits, std::min(8, splits0));
+  const int page_splits = groups_max > 0 ? (groups_max + gps - 1) / gps : 1;
+  constexpr int kTailSplits = 4;
+  if (static_cast<int64_t>(units) * (page_splits + kTailSplits) <= target_wgs) {
+    // few (sequence, kv head) pairs with long page runs: the fp16 tail (up to 127 tokens) goes to 4
+    // workgroups of its own that own no pages, so its work overlaps the page stream instead of
+    // lengthening the workgroups that stream pages (4 x 128K at 1 kv head: 47 -> 38 us with a tail)
+    p.tail_splits = kTailSplits;
+    p.n_splits = page_splits + kTailSplits;
+  } else {
+    // the grid is full: the tail is shared out among the page splits, at least 8 of them where the
+    // grid has room, so that a split's share is about one 16-token chunk
+    p.tail_splits = 0;
+    p.n_splits = std::max(page_splits, std::min(8, splits0));
+  }
   return p;
 }
 

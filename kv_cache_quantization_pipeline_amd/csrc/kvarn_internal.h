@@ -23,6 +23,9 @@ struct DecodePlan {
   int pages_per_group;
   int groups_per_split;
   int n_splits;
+  // 0: the fp16 tail is shared out among all n_splits splits; T > 0: splits 0 .. T-1 own the tail
+  // and no pages, splits T .. n_splits-1 own the pages
+  int tail_splits;
 };
 // ng: quantisation groups per token (1, 2, 4); group_size: query heads per kv head.
 int decode_pages_per_step(int kb, int vb, int ng, int group_size);
