@@ -267,3 +267,17 @@ def test_prepared_calls_match_plain_calls():
     assert states[1][1].tolist() == (st.lens + 3).tolist()
     for x, y in zip(*states):
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+@pytest.mark.parametrize("hkv,extra", [(1, 0), (4, 120)])
+def test_tail_owner_modes_at_share_boundaries(hkv, extra):
+    """Tail lengths at the boundaries of a split's share (0, 1, 31, 32, 33, 127 tokens; 4 tail-only
+    splits own up to 32 each) and a sequence with no full page.  With 1 kv head and 7 sequences the
+    grid has room for tail-only splits; with 4 kv heads and 127 sequences it does not, and the tail is
+    shared out among the page splits.  Against the oracle on the GPU's own cache bytes."""
+    base = [3 * 128, 128 + 1, 2 * 128 + 31, 4 * 128 + 32, 128 + 33, 5 * 128 + 127, 77]
+    lens = base + [(i % 9) * 128 + (i * 37) % 128 for i in range(extra)]
+    st = Setup("kvarn_k4v2_g128", lens, hkv=hkv, hq=8 * hkv, seed=36, max_pages=8)
+    out = st.run_gpu()
+    seqs = list(range(len(base)))
+    _compare(out[seqs], st.run_oracle(seqs), st.lens[seqs])
