@@ -23,8 +23,9 @@
 // workgroup merges its 4 waves x P streams in LDS and writes one split-K
 // partial per query head.
 //
-// The fp16 tail (the len % 128 newest tokens) is shared out among the splits of a (sequence,
-// kv head), in raw-domain sums of their partials.  The workgroups of a pair count their arrivals
+// The fp16 tail (the len % 128 newest tokens) goes to the first splits of a (sequence, kv head):
+// four tail-only splits where the grid has room for them, else a share of every page split; it
+// enters raw-domain sums of their partials.  The workgroups of a pair count their arrivals
 // on a device-scope counter in the workspace; the last one to arrive merges the partials and
 // applies the inverse rotation (combine_head), one wave per query head.
 
@@ -156,7 +157,7 @@ __device__ __forceinline__ void tail_heads(const _Float16* __restrict__ q0, int 
 //   raw domain, only in the first n_tail splits, which own tail tokens),  out = (Hn rot + raw) / L,
 // all zero for an empty sequence.  part: the n_splits partials of this head.  The split loops are
 // unrolled deeply and their loads do not depend on earlier loads, so the rows of many splits are in
-// flight at once (a long sequence with few (sequence, kv head) pairs has ~100 splits).
+// flight at once (a long sequence with few (sequence, kv head) pairs has ~70 splits).
 __device__ __forceinline__ void combine_head(const float* __restrict__ part, int n_splits, int n_tail,
                                              _Float16* __restrict__ o, int lane) {
   float M = -INFINITY;
