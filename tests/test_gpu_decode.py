@@ -281,3 +281,13 @@ def test_tail_owner_modes_at_share_boundaries(hkv, extra):
     out = st.run_gpu()
     seqs = list(range(len(base)))
     _compare(out[seqs], st.run_oracle(seqs), st.lens[seqs])
+
+
+def test_decode_one_sequence_of_a_million_tokens():
+    """One sequence of 2^20 + 37 tokens on one kv head (8192 pages) and 8 query heads: 342 page
+    splits of 12 page groups and 4 tail-only splits, merged by one workgroup; every head against
+    the oracle."""
+    st = Setup("kvarn_k4v2_g128", [(1 << 20) + 37], hkv=1, hq=8, seed=37)
+    assert kv.decode_workspace_bytes(st.fmt, 1, 8, 1, st.max_pages) == 256 + 8 * (342 + 4) * 260 * 4
+    out = st.run_gpu()
+    _compare(out, st.run_oracle(), st.lens)
