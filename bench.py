@@ -648,6 +648,7 @@ def main():
     tq = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev) * 1e-3
     ta = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev) * 1e-3
     td = sum(e[2].elapsed_time(e[3]) for e in ev) / len(ev) * 1e-3
+    med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in ev])) * 1e3 for i in range(3)]
     step_s = elapsed / args.steps
     total_bytes = quant_bytes * args.steps + bytes_app + bytes_dec
     value = total_bytes / elapsed / 1e9
@@ -658,10 +659,10 @@ def main():
     traffic = load_traffic(src_hash)
     kernels = {
         "quantize_tiles": {"GBps": quant_bytes / tq / 1e9, "frac_hbm": quant_bytes / tq / 1e9 / HBM_PEAK_GBPS,
-                           "us": tq * 1e6, "bytes": quant_bytes, "tile_heads": Q_TILES * Q_HKV},
-        "append_token": {"us": ta * 1e6, "bytes": app_b, "GBps": app_b / ta / 1e9},
+                           "us": tq * 1e6, "us_median": med[0], "bytes": quant_bytes, "tile_heads": Q_TILES * Q_HKV},
+        "append_token": {"us": ta * 1e6, "us_median": med[1], "bytes": app_b, "GBps": app_b / ta / 1e9},
         "decode_attention": {"GBps": dec_b / td / 1e9, "frac_hbm": dec_b / td / 1e9 / HBM_PEAK_GBPS,
-                             "us": td * 1e6, "bytes": dec_b, "tokens_per_s": D_B / td,
+                             "us": td * 1e6, "us_median": med[2], "bytes": dec_b, "tokens_per_s": D_B / td,
                              "note": "decode kernel (split-K partials merged by the last workgroup); one layer call, 1 token per sequence"},
         "device_copy": {"us": t_copy * 1e6, "bytes": 2 * n_copy, "GBps": 2 * n_copy / t_copy / 1e9,
                         "frac_hbm": 2 * n_copy / t_copy / 1e9 / HBM_PEAK_GBPS,
