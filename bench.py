@@ -592,14 +592,10 @@ def main():
     host_lens = [np.full(D_B, D_CTX, np.int64) for _ in range(2)]
 
     def decode_bytes(lens):
-        full = lens // 128
-        tail = lens % 128
-        return int((full * D_HKV * R).sum() + (tail * D_HKV * 2 * 256).sum() + D_B * D_HQ * 256 * 2)
+        return _decode_bytes(lens, D_HKV, D_HQ, R)
 
     def append_bytes(lens_before):
-        fills = int(((lens_before + 1) % 128 == 0).sum())
-        base = D_B * D_HKV * (2 * 256 + 2 * 256) + D_B * 8
-        return base + fills * D_HKV * (2 * 128 * 128 * 2 + R)
+        return _append_bytes(lens_before, D_HKV, R)
 
     quant_bytes = Q_TILES * Q_HKV * (2 * 128 * 128 * 2 + R)
     ev = []
