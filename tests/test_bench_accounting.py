@@ -31,3 +31,16 @@ def test_append_bytes_with_and_without_a_fill():
     base = 3 * 4 * 4 * 256 + 3 * 8               # new K/V rows read, tail slots written, lengths
     assert bench._append_bytes(lens, 4, R) == base + 1 * 4 * (2 * 128 * 128 * 2 + R)
     assert bench._append_bytes(np.array([0, 1]), 2, R) == 2 * 2 * 4 * 256 + 2 * 8
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The method needs no cross-GPU exchange and only one GPU is measured: --gpus 2 exits with a
+    message (status 2) before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
