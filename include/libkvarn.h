@@ -84,11 +84,12 @@ kvarn_status kvarn_format_check(const kvarn_format* f);
 /* Bytes of one record (one page of one kv head); 0 if the format is invalid. */
 size_t kvarn_record_bytes(const kvarn_format* f);
 
-/* Workspace bytes kvarn_decode_attention needs for these sizes: one int32 arrival counter per
- * (sequence, kv head), padded to a multiple of 256 bytes, then the split-K partial results (per
- * (sequence, query head, split) a running max, a running sum, a flag, a pad float, 128
- * rotated-domain and 128 raw-domain (fp16 tail) accumulators: 1040 bytes).  The counters must be
- * zero before the first call (see kvarn_decode_attention). */
+/* Workspace bytes kvarn_decode_attention needs for these sizes: the split-K partial results, per
+ * (sequence, query head, split) 128 per-channel sums, a running max, a running sum and two pad floats
+ * (528 bytes), for the fp16-tail split and for every page split (one page split per 4 groups of
+ * pages, a group being 2 pages, or 1 for 16 query heads per kv head, 8-bit codes or groups below 128
+ * channels).  The number of splits depends on the page table's width max_pages_per_seq, which is why
+ * that and the kv-head count are arguments.  0 for an unsupported format or shape. */
 size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t max_pages_per_seq);
 
@@ -134,12 +135,9 @@ kvarn_status kvarn_append_token(const kvarn_format* f, int32_t num_seqs, int32_t
  *              with seq_lens[s] < 128*(max_pages_per_seq + 1); max_pages_per_seq sizes the
  *              split-K grid and the workspace
  *   workspace  (device) >= kvarn_decode_workspace_bytes(...) bytes, 16-byte aligned, owned by the
- *              caller.  It starts with one int32 arrival counter per (sequence, kv head) (the
- *              split-K workgroups of a pair count their arrivals there; the last one merges them),
- *              which must be zero when the call's work starts: zero-fill the workspace once after
- *              allocating it.  Every completed call leaves the counters zero again, so a workspace
- *              can be reused by any later decode call, whatever its shapes.  Calls that may run
- *              at the same time (different streams) need separate workspaces.
+ *              caller.  The call's first kernel writes the split partials there and its second kernel
+ *              merges them, so its contents before and after a call do not matter (no initialisation);
+ *              calls that may run at the same time (different streams) need separate workspaces.
  * Supported query heads per kv head: 1, 2, 4, 8 and 16. */
 kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
                                     int32_t num_kv_heads, const void* q, const void* cache,

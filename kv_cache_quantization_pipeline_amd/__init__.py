@@ -8,7 +8,7 @@ on first use; there is no CPU fallback.
 Functions mirror include/libkvarn.h:
     format_parse, record_bytes, decode_workspace_bytes,
     quantize_tiles, append_token, decode_attention, prefill_attention
-plus decode_workspace (a zero-filled workspace tensor for decode_attention) and
+plus decode_workspace (a workspace tensor for decode_attention) and
 prepare_append_token / prepare_decode_attention (the same calls with their arguments marshalled
 once, for serving loops whose kernels take a few microseconds).
 """
@@ -116,13 +116,13 @@ def decode_workspace_bytes(fmt: Format, num_seqs: int, num_q_heads: int, num_kv_
 
 def decode_workspace(fmt: Format, num_seqs: int, num_q_heads: int, num_kv_heads: int, max_pages_per_seq: int,
                      device=None):
-    """A zero-filled device workspace for decode_attention at these sizes (its arrival counters must
-    start at zero; every decode call leaves them zero, so the tensor can be reused)."""
+    """A device workspace for decode_attention at these sizes (its contents need no initialisation;
+    the tensor can be reused by later calls on the same stream)."""
     import torch
     n = decode_workspace_bytes(fmt, num_seqs, num_q_heads, num_kv_heads, max_pages_per_seq)
     if n == 0:
         raise ValueError("unsupported decode shape")
-    return torch.zeros(n, dtype=torch.uint8, device=device if device is not None else "cuda")
+    return torch.empty(n, dtype=torch.uint8, device=device if device is not None else "cuda")
 
 
 def _ptr(t):
@@ -213,8 +213,8 @@ def _decode_args(fmt, q, cache, page_stride_bytes, page_table, seq_lens, tail_k,
 def decode_attention(fmt: Format, q, cache, page_stride_bytes: int, page_table, seq_lens, tail_k, tail_v,
                      sm_scale: float, out, workspace, num_kv_heads: int, stream=None):
     """q, out: fp16 [B, Hq, 128]; page_table int32 [B, max_pages]; seq_lens int32 [B];
-    tails fp16 [B, Hkv, 128, 128]; workspace: device tensor of >= decode_workspace_bytes bytes whose
-    arrival counters are zero (zero-filled once, e.g. by decode_workspace; each call leaves them zero)."""
+    tails fp16 [B, Hkv, 128, 128]; workspace: device tensor of >= decode_workspace_bytes bytes (any
+    contents, e.g. from decode_workspace)."""
     args = _decode_args(fmt, q, cache, page_stride_bytes, page_table, seq_lens, tail_k, tail_v, sm_scale, out,
                         workspace, num_kv_heads, stream)
     _check(lib().kvarn_decode_attention(*args), "kvarn_decode_attention")

@@ -81,8 +81,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int
   if (!kvarn::decode_supported(f->k_bits, f->v_bits, n_groups(f), G)) return 0;
   const kvarn::DecodePlan plan =
       kvarn::plan_decode(f->k_bits, f->v_bits, n_groups(f), num_seqs, num_kv_heads, G, max_pages_per_seq);
-  return kvarn::decode_counter_bytes(num_seqs, num_kv_heads) +
-         static_cast<size_t>(num_seqs) * num_q_heads * plan.n_splits * kvarn::kPartialFloats * sizeof(float);
+  return kvarn::decode_workspace_bytes(plan, num_seqs, num_q_heads, num_kv_heads);
 }
 
 kvarn_status kvarn_quantize_tiles(const kvarn_format* f, int32_t num_tiles, int32_t num_kv_heads, const void* k,
@@ -147,15 +146,14 @@ kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int
   if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
   const kvarn::DecodePlan plan =
       kvarn::plan_decode(f->k_bits, f->v_bits, n_groups(f), num_seqs, num_kv_heads, G, max_pages_per_seq);
-  if (plan.n_splits > 65535) return KVARN_E_UNSUPPORTED;
+  if (plan.page_splits + 1 > 65535) return KVARN_E_UNSUPPORTED;
   return hip_status(kvarn::launch_decode(f->k_bits, f->v_bits, n_groups(f), G, static_cast<const _Float16*>(q),
                                          static_cast<const uint8_t*>(cache), page_stride_bytes, page_table,
                                          max_pages_per_seq, seq_lens, static_cast<const _Float16*>(tail_k),
                                          static_cast<const _Float16*>(tail_v), sm_scale, static_cast<_Float16*>(out),
-                                         reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                                                  kvarn::decode_counter_bytes(num_seqs, num_kv_heads)),
-                                         static_cast<int*>(workspace), num_seqs, num_q_heads, num_kv_heads, plan,
-                                         stream));
+                                         kvarn::decode_workspace_layout(workspace, plan, num_seqs, num_q_heads,
+                                                                        num_kv_heads),
+                                         num_seqs, num_q_heads, num_kv_heads, plan, stream));
 }
 
 kvarn_status kvarn_prefill_attention(const kvarn_format* f, int32_t num_seqs, int32_t max_q, int32_t num_q_heads,

@@ -60,11 +60,11 @@ def test_record_and_workspace_sizes():
     assert kv.record_bytes(kv.format_parse("kvarn_k8v8_g128")) == 35840
     assert kv.record_bytes(kv.format_parse("kvarn_k4v2_g64")) == 17408     # + c, s'[2], m'[2] per half
     assert kv.record_bytes(kv.format_parse("kvarn_k4v2_g32")) == 21504     # + c, s'[4], m'[4] per half
-    ws = kv.decode_workspace_bytes(f, 32, 32, 4, 128)
-    # 32 x 4 int32 arrival counters (512 B, a multiple of 256), then 260 floats per (seq, q head, split)
-    assert ws > 512 and (ws - 512) % (32 * 32 * 260 * 4) == 0
-    # 9 counters padded to 256 B; one page split plus 4 tail-only splits (the grid has room for them)
-    assert kv.decode_workspace_bytes(f, 3, 3, 3, 1) == 256 + 3 * 3 * 5 * 260 * 4
+    # B 32 x 128 pages, 8 query heads per kv head: 64 two-page groups per sequence, one per wave, so
+    # 16 page splits of 4 waves plus the tail split; 132 floats per (seq, q head, split)
+    assert kv.decode_workspace_bytes(f, 32, 32, 4, 128) == 32 * 32 * (1 + 16) * 132 * 4
+    # one page split and the tail split
+    assert kv.decode_workspace_bytes(f, 3, 3, 3, 1) == 3 * 3 * 2 * 132 * 4
     assert kv.decode_workspace_bytes(f, 32, 24, 4, 128) == 0   # G = 6 unsupported
     for G in (1, 2, 4, 8, 16):
         assert kv.decode_workspace_bytes(f, 4, 2 * G, 2, 16) > 0
