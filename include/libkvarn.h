@@ -63,7 +63,9 @@ typedef enum {
   KVARN_OK = 0,
   KVARN_E_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes */
   KVARN_E_UNSUPPORTED = 2, /* a format, block size, head size or GQA ratio this build does not run */
-  KVARN_E_HIP = 3          /* a HIP launch or runtime call failed */
+  KVARN_E_HIP = 3,         /* a HIP launch or runtime call failed */
+  KVARN_E_SCRATCH_LIMIT = 4 /* kvarn_decode_attention_noalloc: the call needs more workspace than its
+                               fixed scratch holds (kvarn_decode_noalloc_max_workspace_bytes) */
 } kvarn_status;
 
 /* kv-cache dtype string "kvarn_k{K}v{V}_g{G}" ([HYPHO] section "工程实践：一行配置启用";
@@ -146,6 +148,26 @@ kvarn_status kvarn_decode_attention(const kvarn_format* f, int32_t num_seqs, int
                                     const void* tail_k, const void* tail_v,
                                     float sm_scale, void* out, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/* kvarn_decode_attention without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The split
+ * partials go to a fixed array of kvarn_decode_noalloc_max_workspace_bytes() bytes (64 MiB) that the
+ * library holds on each GPU it runs on until the process ends; the call allocates nothing and takes
+ * that array's address once per device (with the device current) on its first call there.
+ * Arguments and results as for kvarn_decode_attention.  A call whose
+ * kvarn_decode_workspace_bytes(...) exceeds the array returns KVARN_E_SCRATCH_LIMIT and launches
+ * nothing.  Every call on one GPU shares the array: calls that may overlap on one GPU (different
+ * streams, or different host threads without ordering) race and must not be issued; calls on one
+ * stream are ordered and safe.  The array holds nothing between calls (no initialisation needed). */
+kvarn_status kvarn_decode_attention_noalloc(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, const void* q, const void* cache,
+                                            int64_t page_stride_bytes, const int32_t* page_table,
+                                            int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                            const void* tail_k, const void* tail_v, float sm_scale, void* out,
+                                            hipStream_t stream);
+
+/* Bytes of the fixed scratch array of kvarn_decode_attention_noalloc (64 MiB). */
+size_t kvarn_decode_noalloc_max_workspace_bytes(void);
 
 /* Chunked prefill attention over the quantised cache: many queries per kv head at once, the phase
  * before decoding ([HYPHO] section "它怎么做到的：四步流水线" for the cache it reads; scales folded

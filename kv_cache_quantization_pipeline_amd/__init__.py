@@ -20,7 +20,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvarn.so")
 
-KVARN_OK, KVARN_E_INVALID_ARG, KVARN_E_UNSUPPORTED, KVARN_E_HIP = 0, 1, 2, 3
+KVARN_OK, KVARN_E_INVALID_ARG, KVARN_E_UNSUPPORTED, KVARN_E_HIP, KVARN_E_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 
 # every C-ABI entry point declared in include/libkvarn.h
 EXPORTS = (
@@ -31,6 +31,8 @@ EXPORTS = (
     "kvarn_quantize_tiles",
     "kvarn_append_token",
     "kvarn_decode_attention",
+    "kvarn_decode_attention_noalloc",
+    "kvarn_decode_noalloc_max_workspace_bytes",
     "kvarn_prefill_attention",
     "kvarn_status_string",
 )
@@ -80,6 +82,11 @@ def lib():
         L.kvarn_decode_attention.restype = i32
         L.kvarn_decode_attention.argtypes = [fp, i32, i32, i32, vp, vp, i64, vp, i32, vp, vp, vp, flt, vp, vp, sz,
                                              vp]
+        L.kvarn_decode_attention_noalloc.restype = i32
+        L.kvarn_decode_attention_noalloc.argtypes = [fp, i32, i32, i32, vp, vp, i64, vp, i32, vp, vp, vp, flt, vp,
+                                                     vp]
+        L.kvarn_decode_noalloc_max_workspace_bytes.restype = sz
+        L.kvarn_decode_noalloc_max_workspace_bytes.argtypes = []
         L.kvarn_prefill_attention.restype = i32
         L.kvarn_prefill_attention.argtypes = [fp, i32, i32, i32, i32, vp, vp, vp, i64, vp, i32, vp, vp, vp, flt, vp,
                                               vp]
@@ -197,14 +204,14 @@ def _decode_args(fmt, q, cache, page_stride_bytes, page_table, seq_lens, tail_k,
     _need(seq_lens, "seq_lens", torch.int32, 1)
     _need(tail_k, "tail_k", torch.float16, 4)
     _need(tail_v, "tail_v", torch.float16, 4)
-    if not workspace.is_cuda or not workspace.is_contiguous():
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous device tensor")
     B, hq = q.shape[0], q.shape[1]
     if out.shape != q.shape or seq_lens.shape[0] != B or page_table.shape[0] != B:
         raise ValueError("inconsistent shapes for decode_attention")
     if tuple(tail_k.shape) != (B, num_kv_heads, 128, 128) or tail_v.shape != tail_k.shape:
         raise ValueError(f"tails must be [B, Hkv, 128, 128], got {tuple(tail_k.shape)}")
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return (ctypes.byref(fmt), B, hq, num_kv_heads, _ptr(q), _ptr(cache), page_stride_bytes, _ptr(page_table),
             page_table.shape[1], _ptr(seq_lens), _ptr(tail_k), _ptr(tail_v), float(sm_scale), _ptr(out),
             _ptr(workspace), ws_bytes, _stream(stream))
@@ -218,6 +225,20 @@ def decode_attention(fmt: Format, q, cache, page_stride_bytes: int, page_table, 
     args = _decode_args(fmt, q, cache, page_stride_bytes, page_table, seq_lens, tail_k, tail_v, sm_scale, out,
                         workspace, num_kv_heads, stream)
     _check(lib().kvarn_decode_attention(*args), "kvarn_decode_attention")
+
+
+def decode_attention_noalloc(fmt: Format, q, cache, page_stride_bytes: int, page_table, seq_lens, tail_k, tail_v,
+                             sm_scale: float, out, num_kv_heads: int, stream=None):
+    """decode_attention with the library's fixed per-GPU scratch instead of a caller workspace (for
+    callers that cannot allocate); calls that may overlap on one GPU race."""
+    args = _decode_args(fmt, q, cache, page_stride_bytes, page_table, seq_lens, tail_k, tail_v, sm_scale, out,
+                        None, num_kv_heads, stream)
+    args = args[:14] + args[16:]
+    _check(lib().kvarn_decode_attention_noalloc(*args), "kvarn_decode_attention_noalloc")
+
+
+def decode_noalloc_max_workspace_bytes() -> int:
+    return int(lib().kvarn_decode_noalloc_max_workspace_bytes())
 
 
 class PreparedCall:

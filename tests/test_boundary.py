@@ -130,6 +130,30 @@ def test_calls_reject_bad_arguments_before_launch():
     del args
 
 
+def test_noalloc_decode_rejects_before_launch():
+    """The no-allocation decode entry point checks its arguments like the workspace one, and a call
+    whose workspace would exceed its fixed 64 MiB scratch returns KVARN_E_SCRATCH_LIMIT before any
+    HIP call (so no GPU is needed here)."""
+    L = kv.lib()
+    f = kv.format_parse("kvarn_k4v2_g128")
+    fp = ctypes.byref(f)
+    dummy = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+    R = 15360
+    assert L.kvarn_decode_noalloc_max_workspace_bytes() == 64 << 20
+
+    def dec(nseq=2, hq=16, hkv=2, maxp=4, q=dummy):
+        return L.kvarn_decode_attention_noalloc(fp, nseq, hq, hkv, q, dummy, hkv * R, dummy, maxp, dummy, dummy, dummy,
+                                                0.1, dummy, None)
+    assert dec(hq=15) == kv.KVARN_E_INVALID_ARG
+    assert dec(hq=12) == kv.KVARN_E_UNSUPPORTED
+    assert dec(q=None) == kv.KVARN_E_INVALID_ARG
+    assert dec(nseq=0) == kv.KVARN_OK
+    # 64 sequences x 32 query heads over a 20000-page table: 2501 splits x 528 bytes each, ~2.7 GB
+    assert kv.decode_workspace_bytes(f, 64, 32, 4, 20000) > 64 << 20
+    assert dec(nseq=64, hq=32, hkv=4, maxp=20000) == kv.KVARN_E_SCRATCH_LIMIT
+    assert "scratch" in kv.status_string(kv.KVARN_E_SCRATCH_LIMIT)
+
+
 def test_prefill_rejects_before_launch():
     L = kv.lib()
     f = kv.format_parse("kvarn_k4v2_g128")
