@@ -179,6 +179,8 @@ def _append_args(fmt, k_new, v_new, seq_lens, tail_k, tail_v, page_table, cache,
     _need(page_table, "page_table", torch.int32, 2)
     _need(cache, "cache", torch.uint8)
     B, hkv = k_new.shape[0], k_new.shape[1]
+    if k_new.shape[2] != 128:
+        raise ValueError(f"k_new must be [B, Hkv, 128] (head_dim 128), got {tuple(k_new.shape)}")
     if (v_new.shape != k_new.shape or tuple(tail_k.shape) != (B, hkv, 128, 128) or tail_v.shape != tail_k.shape
             or seq_lens.shape[0] != B or page_table.shape[0] != B):
         raise ValueError("inconsistent shapes for append_token")
@@ -207,6 +209,8 @@ def _decode_args(fmt, q, cache, page_stride_bytes, page_table, seq_lens, tail_k,
     if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous device tensor")
     B, hq = q.shape[0], q.shape[1]
+    if q.shape[2] != 128:
+        raise ValueError(f"q must be [B, Hq, 128] (head_dim 128), got {tuple(q.shape)}")
     if out.shape != q.shape or seq_lens.shape[0] != B or page_table.shape[0] != B:
         raise ValueError("inconsistent shapes for decode_attention")
     if tuple(tail_k.shape) != (B, num_kv_heads, 128, 128) or tail_v.shape != tail_k.shape:

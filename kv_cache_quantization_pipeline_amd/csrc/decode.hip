@@ -460,6 +460,25 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
       }
       m_col = rows_max4(mloc);
       const bool live = valid_own && m_col != -INFINITY;
+      // The weights w_t = p_t s'_t go to the MFMA in fp16.  So that they stay in fp16's normal range
+      // whatever the magnitude of V, the softmax of the column is taken against m + E, with 2^E the
+      // power of two at or below the page's largest V token scale: then w_t <= 2.  The column's state
+      // (m + E, sum_t p_t 2^-E, sums 2^-E) is the same online-softmax state with a shifted reference.
+      int e_pow[P];
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        const float* sv = stg + e * SC + HS + kCh;  // s'_V of page e, NG x 128 floats
+        float smax = 0.f;
+#pragma unroll
+        for (int k = 0; k < 2 * NG; ++k) smax = fmaxf(smax, sv[lane + 64 * k]);
+        smax = rows_max4(row_max16(smax));
+        const int ex = smax > 0.f ? __builtin_amdgcn_frexp_expf(smax) - 1 : 0;
+        e_pow[e] = min(max(ex, -100), 100);
+      }
+      int e_col = e_pow[0];
+#pragma unroll
+      for (int e = 1; e < P; ++e) e_col = e_oc == e ? e_pow[e] : e_col;
+      const float m_ref = m_col + static_cast<float>(e_col);
 
       f16x8 C0N;
       constexpr float c0 = 0.5f * ((1 << VB) - 1);
@@ -473,7 +492,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[mb][i] = live ? __builtin_amdgcn_exp2f(lg[mb][i] - m_col) : 0.f;
+          pr[mb][i] = live ? __builtin_amdgcn_exp2f(lg[mb][i] - m_ref) : 0.f;
           psum += pr[mb][i];
         }
       l_lane = psum;
@@ -536,6 +555,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
           acc[nb][3] = cv.w * c[3];
         }
       }
+      m_col = m_ref;  // the reference the column's sums are taken against
     }
 
     // ---- merge the 4 waves x P streams of each head, write one partial per head ----------------

@@ -26,6 +26,8 @@ namespace kvarn {
 namespace {
 
 constexpr int kRowsPerBlock = 64;  // 4 waves x 16 query rows
+// Smallest divisor of a row's PV weights on one page (see the weight rescale below).
+constexpr float kMinWeightScale = 1e-30f;
 
 // Position of tail token t in a row of the transposed LDS copy of the tail V: k-step t / 32, lane
 // row (t >> 2) & 3, slot 2 (t & 3) + ((t >> 4) & 1), the slot order of the PV weights below.
@@ -234,8 +236,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
         wmax = fmaxf(wmax, wv[mb][i]);
       }
     }
+    // (bounded below: where every weight on the page is that small, the page is negligible against
+    // the row's running sum, and 1 / wmax must not overflow; the weights then round to fp16 zeros)
     wmax = rows_max4(wmax);
-    const float wscale = wmax > 0.f ? wmax : 1.0f;
+    const float wscale = fmaxf(wmax, kMinWeightScale);
     const float inv_ws = 1.0f / wscale;
     msum *= inv_ws;
     f16x8 aw[4];
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
           wmax = fmaxf(wmax, pr[mb][i]);
         }
       wmax = rows_max4(wmax);
-      const float wscale = wmax > 0.f ? wmax : 1.0f;
+      const float wscale = fmaxf(wmax, kMinWeightScale);
       const float inv_ws = 1.0f / wscale;
       f16x8 aw[4];
 #pragma unroll

@@ -177,3 +177,36 @@ def test_status_strings():
     assert kv.status_string(0) == "ok"
     assert kv.status_string(3) == "HIP error"
     assert kv.status_string(99) == "unknown status"
+
+
+def test_binding_rejects_head_dim_other_than_128():
+    """The kernels assume 128 channels: the binding checks the last dimension of q / k_new / v_new
+    before any C-ABI call (the tensors are never touched on the device, so CPU fakes suffice)."""
+    torch = pytest.importorskip("torch")
+
+    class FakeCuda:
+        """Stands in for a device tensor in the binding's checks (never passed to the library)."""
+        def __init__(self, shape, dtype):
+            self.shape, self.dtype, self.is_cuda = torch.Size(shape), dtype, True
+
+        def is_contiguous(self):
+            return True
+
+        def dim(self):
+            return len(self.shape)
+
+    orig = torch.Tensor
+    try:
+        torch.Tensor = FakeCuda   # isinstance checks in the binding accept the fakes
+        f = kv.format_parse("kvarn_k4v2_g128")
+        h, i32, u8 = torch.float16, torch.int32, torch.uint8
+        with pytest.raises(ValueError, match="head_dim"):
+            kv._decode_args(f, FakeCuda((2, 8, 64), h), FakeCuda((100,), u8), 15360, FakeCuda((2, 4), i32),
+                            FakeCuda((2,), i32), FakeCuda((2, 1, 128, 128), h), FakeCuda((2, 1, 128, 128), h), 0.1,
+                            FakeCuda((2, 8, 64), h), FakeCuda((100,), u8), 1, None)
+        with pytest.raises(ValueError, match="head_dim"):
+            kv._append_args(f, FakeCuda((2, 1, 64), h), FakeCuda((2, 1, 64), h), FakeCuda((2,), i32),
+                            FakeCuda((2, 1, 128, 128), h), FakeCuda((2, 1, 128, 128), h), FakeCuda((2, 4), i32),
+                            FakeCuda((100,), u8), 15360, None)
+    finally:
+        torch.Tensor = orig
