@@ -55,5 +55,23 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+# stand-alone timing programs (not part of the library), built into <repo>/_build/
+PROBES = [("probes/rotation_probe.hip", "rotation_probe")]
+
+
+def build_probes(verbose: bool = False) -> list:
+    out_dir = os.path.join(ROOT, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    outs = []
+    for src, name in PROBES:
+        out = os.path.join(out_dir, name)
+        _run(["hipcc", "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
+              "-packed-fp32-ops", "-o", out, os.path.join(HERE, src)], verbose)
+        outs.append(out)
+    return outs
+
+
 if __name__ == "__main__":
     build(verbose="-v" in sys.argv)
+    if "--probes" in sys.argv:
+        build_probes(verbose="-v" in sys.argv)

@@ -597,27 +597,33 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
   }
 }
 
-// Merge of the split partials of one (sequence, query head) per workgroup: wave w folds page splits
-// 1 + w, 5 + w, ... (rotated domain) with an online rescale, 16 splits' rows in flight at a time, and
-// wave 0 also takes the tail split 0 (raw domain).  With M the largest running max and
+// Merge of the split partials of one (sequence, query head) per workgroup of 8 waves: wave w folds
+// page splits 1 + w, 9 + w, ... (rotated domain) with an online rescale, 16 splits' rows in flight at
+// a time, and wave 0 also reads the tail split 0 (raw domain) before its batches.  With M the largest running max and
 // f_k = exp2(M_k - M): L = sum_k f_k L_k, out = (Hn sum_k f_k rot_k + f_0 raw_0) / L; all zero for an
 // empty sequence.  Lane l owns output channels 2l, 2l + 1.
-__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part, int n_splits,
+__global__ __launch_bounds__(512) void decode_merge_kernel(const float* __restrict__ part, int n_splits,
                                                            _Float16* __restrict__ out) {
-  constexpr int kBatch = 16;
-  __shared__ float2 wacc[4][64];
-  __shared__ float2 wml[4];
+  constexpr int kBatch = 16, kW = 8;
+  __shared__ float2 wacc[kW][64];
+  __shared__ float2 wml[kW];
   const int hq = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float* ph = part + static_cast<int64_t>(hq) * n_splits * kPartFloats;
+  // wave 0 also reads the tail split's partial, before the batches
+  float2 tml = make_float2(-INFINITY, 0.f), traw = make_float2(0.f, 0.f);
+  if (wave == 0) {
+    tml = *reinterpret_cast<const float2*>(ph + kSumOff);
+    traw = *reinterpret_cast<const float2*>(ph + 2 * lane);
+  }
 
   float M = -INFINITY, L = 0.f, r0 = 0.f, r1 = 0.f;
-  for (int k0 = 1 + wave; k0 < n_splits; k0 += 4 * kBatch) {
+  for (int k0 = 1 + wave; k0 < n_splits; k0 += kW * kBatch) {
     float2 ml[kBatch], a[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int k = k0 + 4 * u;
+      const int k = k0 + kW * u;
       if (k < n_splits) {
         ml[u] = *reinterpret_cast<const float2*>(ph + k * kPartFloats + kSumOff);
         a[u] = *reinterpret_cast<const float2*>(ph + k * kPartFloats + 2 * lane);
@@ -649,15 +655,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   __syncthreads();
   if (wave != 0) return;
 
-  const float2 tml = *reinterpret_cast<const float2*>(ph + kSumOff);
-  const float2 traw = *reinterpret_cast<const float2*>(ph + 2 * lane);
   float Mt = tml.x;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, wml[w].x);
+  for (int w = 0; w < kW; ++w) Mt = fmaxf(Mt, wml[w].x);
   float Lt = 0.f, r[2] = {0.f, 0.f}, raw[2] = {0.f, 0.f};
   if (Mt != -INFINITY) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kW; ++w) {
       const float f = __builtin_amdgcn_exp2f(wml[w].x - Mt);
       Lt = fmaf(wml[w].y, f, Lt);
       r[0] = fmaf(wacc[w][lane].x, f, r[0]);
@@ -702,7 +706,7 @@ static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64
                      ws.part, plan.page_splits, tail_k, tail_v, sm_scale * kLog2e);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_seqs * num_q_heads), dim3(256), 0, stream, ws.part,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_seqs * num_q_heads), dim3(512), 0, stream, ws.part,
                      plan.page_splits + 1, out);
   return hipGetLastError();
 }
