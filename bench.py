@@ -7,19 +7,22 @@ One step = one pass of the whole path over one batch of synthetic input:
   2. kvarn_append_token     one new token for each of 32 sequences x 4 kv heads (fp16 tail; a tail that
                             fills is quantised inline)
   3. kvarn_decode_attention decode for 32 sequences at 16384+ tokens, 32 query / 4 kv heads, over the
-                            k4v2 paged cache plus the fp16 tails (one kernel: split-K, then the last workgroup merges)
+                            k4v2 paged cache plus the fp16 tails (two kernels: split-K partials over
+                            the pages and the tail, then one merge per (sequence, query head))
 Inputs are resident in HBM before the timed region.  Two copies of every input and cache are used
 alternately, so each kernel's reads come from HBM, not from the 256 MB Infinity Cache.
 
 Prints one JSON line.  value = algorithmic bytes of the step / step time (GB/s); the per-kernel
-numbers (quantize GB/s, decode tokens/s, fractions of the 8 TB/s HBM peak) are in "kernels".
+numbers (quantize GB/s, decode tokens/s, fractions of the 8 TB/s HBM peak) are in "kernels", with
+the decode also timed on its own (back-to-back calls over rotated cache copies) and the long-context
+serving loop (4 sequences x 128K tokens, 8 query / 1 kv head, append + decode per step, five cache
+copies in turn; eager and HIP-graph replay) after the timed steps.
 
 --variants (a separate run, not the step): the same quantise and decode workloads in the grouped
 formats k4v2 g64 / g32; chunked prefill (4 sequences, a 512-token chunk on top of 16384 cached
-tokens, 32 query / 4 kv heads, k4v2 g128) against the fp16 MFMA peak; the long-context serving loop
-(4 sequences x 128K tokens, 8 query / 1 kv head, append + decode per step, five cache copies in turn);
-and the ragged continuous-batching step (64 sequences of 1K-32K tokens, k4v2 and k8v8 pools); one JSON
-line of its own.
+tokens, 32 query / 4 kv heads, k4v2 g128) against the fp16 MFMA peak; and the ragged
+continuous-batching step (64 sequences of 1K-32K tokens, k4v2 and k8v8 pools); one JSON line of its
+own.
 """
 import argparse
 import hashlib
@@ -332,7 +335,8 @@ def long_context_steps(kv, synth, dev):
     decode per copy (the last append of each copy fills the tail and quantises it inline).  The cache
     is 63 MB, so five independent copies (315 MB) are used in turn and every read comes from HBM,
     not from the 256 MB Infinity Cache.  Timed with HIP events on the launch stream around each call;
-    the calls are prepared (marshalled once), so that the host keeps ahead of the GPU."""
+    the calls are prepared (marshalled once), so that the host keeps ahead of the GPU.  Then the same
+    steps are captured as one HIP graph per copy and timed by replay (no host launch cost per call)."""
     import numpy as np
     import torch
     w = synth.WORKLOADS["decode_long_b4_ctx128k"]
@@ -411,10 +415,41 @@ def long_context_steps(kv, synth, dev):
         b_dec += _decode_bytes(lb + 1, hkv, hq, R)
     b_app, b_dec = b_app / n_steps, b_dec / n_steps
     step = elapsed / n
+
+    # the same 128 steps per copy captured once as a HIP graph (append + decode, 256 launches) and
+    # replayed, each copy reset to its starting state first; timed with events around each replay
+    graphs = []
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    for c in range(n_copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for s in range(n_steps):
+                kv.append_token(fmt, knew[s], vnew[s], lens[c], tails[c][0], tails[c][1], pt, caches[c], stride)
+                kv.decode_attention(fmt, q, caches[c], stride, pt, lens[c], tails[c][0], tails[c][1], sm, out, ws,
+                                    hkv)
+        graphs.append(g)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    ge = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_copies)]
+    for c in range(n_copies):
+        lens[c].fill_(ctx)
+        tails[c][0].zero_()
+        tails[c][1].zero_()
+    torch.cuda.synchronize(dev)
+    for c in range(n_copies):
+        ge[c][0].record()
+        graphs[c].replay()
+        ge[c][1].record()
+    torch.cuda.synchronize(dev)
+    assert lens[0].cpu().tolist() == [ctx + n_steps] * B
+    g_step = sum(e[0].elapsed_time(e[1]) for e in ge) * 1e-3 / (n_copies * n_steps)
+    del graphs
     return {"workload": f"{B} seqs x {ctx}+ tokens, {hq} q / {hkv} kv heads, {FORMAT}, {n_steps} append + decode "
                         f"steps on each of {n_copies} cache copies (one tail fill per sequence per copy)",
             "us_per_step": step * 1e6, "tokens_per_s": B / step, "step_GBps": (b_app + b_dec) / step / 1e9,
             "step_frac_hbm": (b_app + b_dec) / step / 1e9 / HBM_PEAK_GBPS,
+            "graph_us_per_step": g_step * 1e6, "graph_tokens_per_s": B / g_step,
+            "graph_step_frac_hbm": (b_app + b_dec) / g_step / 1e9 / HBM_PEAK_GBPS,
             "decode_us": td * 1e6, "decode_us_median": td_med * 1e6, "decode_bytes": b_dec,
             "decode_GBps": b_dec / td_med / 1e9, "decode_frac_hbm": b_dec / td_med / 1e9 / HBM_PEAK_GBPS,
             "decode_tokens_per_s": B / td_med,

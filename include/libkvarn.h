@@ -64,8 +64,9 @@ typedef enum {
   KVARN_E_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes */
   KVARN_E_UNSUPPORTED = 2, /* a format, block size, head size or GQA ratio this build does not run */
   KVARN_E_HIP = 3,         /* a HIP launch or runtime call failed */
-  KVARN_E_SCRATCH_LIMIT = 4 /* kvarn_decode_attention_noalloc: the call needs more workspace than its
-                               fixed scratch holds (kvarn_decode_noalloc_max_workspace_bytes) */
+  KVARN_E_SCRATCH_LIMIT = 4, /* kvarn_decode_attention_noalloc: the call needs more workspace than its
+                                fixed scratch holds (kvarn_decode_noalloc_max_workspace_bytes) */
+  KVARN_E_OUT_OF_PAGES = 5   /* kvarn_page_pool_reserve: the pool has fewer free pages than the batch needs */
 } kvarn_status;
 
 /* kv-cache dtype string "kvarn_k{K}v{V}_g{G}" ([HYPHO] section "工程实践：一行配置启用";
@@ -115,7 +116,11 @@ kvarn_status kvarn_quantize_tiles(const kvarn_format* f, int32_t num_tiles, int3
  *   seq_lens      (device) int32 [num_seqs], read then incremented
  *   tail_k/tail_v (device) fp16 [num_seqs][num_kv_heads][128][head_dim]
  *   page_table    (device) int32 [num_seqs][max_pages_per_seq]
- * The page for a filling tile must be allocated in page_table before the call.
+ * The page for a filling tile must be allocated in page_table before the call
+ * (kvarn_page_pool_reserve for the length after the call does that).
+ * The pages fix the per-tile quantiser but not when a decode step's new token is quantised; keeping
+ * a tile's newest tokens in fp16 and quantising the tile once its 128th token arrives (so every
+ * record is a whole tile, as the bulk path writes it) is this library's reading.
  * One launch reads and advances the lengths: while it runs, seq_lens[s] holds the number of kv
  * heads already appended in its bits 24 and up, so lengths must stay below 2^24 tokens, at most
  * 64 kv heads are supported (more return KVARN_E_UNSUPPORTED), and nothing else may read seq_lens
@@ -190,6 +195,41 @@ kvarn_status kvarn_prefill_attention(const kvarn_format* f, int32_t num_seqs, in
                                      const int32_t* page_table, int32_t max_pages_per_seq,
                                      const int32_t* seq_lens, const void* tail_k, const void* tail_v,
                                      float sm_scale, void* out, hipStream_t stream);
+
+/* Host-side page pool for the paged cache (block_size 128, [HYPHO] section "工程实践：一行配置启用";
+ * [LEHUY] section "Dễ dàng tích hợp và sử dụng").  It hands out physical page ids 0 .. num_pages-1 of
+ * the caller's cache pool (page_stride_bytes each) and fills the host copy of the page table that the
+ * caller then uploads; it touches no device memory and makes no HIP call.  A sequence of length L
+ * needs pages for its full tiles 0 .. L/128 - 1 only (the L % 128 newest tokens are in the fp16 tail).
+ * Calls on one pool may come from several host threads (each call holds the pool's lock). */
+typedef struct kvarn_page_pool kvarn_page_pool;
+
+/* New pool of num_pages free pages (num_pages >= 0); *pool receives it.  KVARN_E_INVALID_ARG for a null
+ * out pointer, a negative count or a failed host allocation. */
+kvarn_status kvarn_page_pool_create(int32_t num_pages, kvarn_page_pool** pool);
+
+/* Free the pool (null is ignored).  Page tables filled from it keep their ids. */
+void kvarn_page_pool_destroy(kvarn_page_pool* pool);
+
+/* Free pages left; -1 for a null pool. */
+int32_t kvarn_page_pool_num_free(kvarn_page_pool* pool);
+
+/* Give every sequence of a batch the pages its new length needs.  For each s, the row
+ * page_table[s*max_pages_per_seq ...] (host) holds num_owned[s] (host, in/out) pages owned by the
+ * sequence in entries 0 .. num_owned[s]-1; entries num_owned[s] .. new_lens[s]/128 - 1 receive new
+ * pages and num_owned[s] becomes new_lens[s]/128 when that is larger (a shorter length keeps its
+ * pages).  All or nothing: on KVARN_E_OUT_OF_PAGES (too few free pages for the whole batch) or
+ * KVARN_E_INVALID_ARG (negative sizes, num_owned[s] > max_pages_per_seq, new_lens[s]/128 >
+ * max_pages_per_seq) nothing changes.  For decode steps replayed without returning to the host (a
+ * captured graph), reserve for the length after the last replayed step. */
+kvarn_status kvarn_page_pool_reserve(kvarn_page_pool* pool, int32_t num_seqs, const int32_t* new_lens,
+                                     int32_t* page_table, int32_t max_pages_per_seq, int32_t* num_owned);
+
+/* Return the *num_owned pages of one sequence's row (host) to the pool, set those entries to -1 and
+ * *num_owned to 0.  KVARN_E_INVALID_ARG, changing nothing, if an entry is not a page this pool handed
+ * out and has not taken back, or appears twice. */
+kvarn_status kvarn_page_pool_release(kvarn_page_pool* pool, int32_t* page_table_row, int32_t max_pages_per_seq,
+                                     int32_t* num_owned);
 
 /* Human-readable name of a status. */
 const char* kvarn_status_string(kvarn_status s);

@@ -7,7 +7,8 @@ on first use; there is no CPU fallback.
 
 Functions mirror include/libkvarn.h:
     format_parse, record_bytes, decode_workspace_bytes,
-    quantize_tiles, append_token, decode_attention, prefill_attention
+    quantize_tiles, append_token, decode_attention, prefill_attention,
+    decode_attention_noalloc, PagePool (kvarn_page_pool_*)
 plus decode_workspace (a workspace tensor for decode_attention) and
 prepare_append_token / prepare_decode_attention (the same calls with their arguments marshalled
 once, for serving loops whose kernels take a few microseconds).
@@ -20,7 +21,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvarn.so")
 
-KVARN_OK, KVARN_E_INVALID_ARG, KVARN_E_UNSUPPORTED, KVARN_E_HIP, KVARN_E_SCRATCH_LIMIT = 0, 1, 2, 3, 4
+KVARN_OK, KVARN_E_INVALID_ARG, KVARN_E_UNSUPPORTED, KVARN_E_HIP, KVARN_E_SCRATCH_LIMIT, KVARN_E_OUT_OF_PAGES = range(6)
 
 # every C-ABI entry point declared in include/libkvarn.h
 EXPORTS = (
@@ -34,6 +35,11 @@ EXPORTS = (
     "kvarn_decode_attention_noalloc",
     "kvarn_decode_noalloc_max_workspace_bytes",
     "kvarn_prefill_attention",
+    "kvarn_page_pool_create",
+    "kvarn_page_pool_destroy",
+    "kvarn_page_pool_num_free",
+    "kvarn_page_pool_reserve",
+    "kvarn_page_pool_release",
     "kvarn_status_string",
 )
 
@@ -90,6 +96,16 @@ def lib():
         L.kvarn_prefill_attention.restype = i32
         L.kvarn_prefill_attention.argtypes = [fp, i32, i32, i32, i32, vp, vp, vp, i64, vp, i32, vp, vp, vp, flt, vp,
                                               vp]
+        L.kvarn_page_pool_create.restype = i32
+        L.kvarn_page_pool_create.argtypes = [i32, ctypes.POINTER(vp)]
+        L.kvarn_page_pool_destroy.restype = None
+        L.kvarn_page_pool_destroy.argtypes = [vp]
+        L.kvarn_page_pool_num_free.restype = i32
+        L.kvarn_page_pool_num_free.argtypes = [vp]
+        L.kvarn_page_pool_reserve.restype = i32
+        L.kvarn_page_pool_reserve.argtypes = [vp, i32, vp, vp, i32, vp]
+        L.kvarn_page_pool_release.restype = i32
+        L.kvarn_page_pool_release.argtypes = [vp, vp, i32, vp]
         L.kvarn_status_string.restype = ctypes.c_char_p
         L.kvarn_status_string.argtypes = [i32]
         _lib = L
@@ -303,3 +319,57 @@ def prefill_attention(fmt: Format, q, q_lens, cache, page_stride_bytes: int, pag
                                        _stream(stream))
     _check(st, "kvarn_prefill_attention")
 
+
+
+class PagePool:
+    """kvarn_page_pool: host-side pool of 128-token cache pages.  Page tables and ownership counts are
+    numpy int32 arrays on the host, filled in place (upload the table to the device afterwards)."""
+
+    def __init__(self, num_pages: int):
+        h = ctypes.c_void_p()
+        _check(lib().kvarn_page_pool_create(num_pages, ctypes.byref(h)), "kvarn_page_pool_create")
+        self._h = h
+        self.num_pages = num_pages
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            lib().kvarn_page_pool_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().kvarn_page_pool_num_free(self._h))
+
+    @staticmethod
+    def _i32(a, name, ndim):
+        import numpy as np
+        if not isinstance(a, np.ndarray) or a.dtype != np.int32 or a.ndim != ndim or not a.flags.c_contiguous:
+            raise ValueError(f"{name} must be a C-contiguous numpy int32 array with {ndim} dims")
+        return a.ctypes.data_as(ctypes.c_void_p)
+
+    def reserve(self, new_lens, page_table, num_owned):
+        """new_lens int32 [B]; page_table int32 [B, max_pages] and num_owned int32 [B], both updated."""
+        B = new_lens.shape[0] if hasattr(new_lens, "shape") else 0
+        pl, pt, po = (self._i32(new_lens, "new_lens", 1), self._i32(page_table, "page_table", 2),
+                      self._i32(num_owned, "num_owned", 1))
+        if page_table.shape[0] != B or num_owned.shape[0] != B:
+            raise ValueError("inconsistent batch sizes for reserve")
+        _check(lib().kvarn_page_pool_reserve(self._h, B, pl, pt, page_table.shape[1], po), "kvarn_page_pool_reserve")
+
+    def release(self, page_table_row, num_owned, s: int = 0):
+        """Return sequence s's pages: page_table_row is the int32 [max_pages] row (or the [B, max_pages] table
+        with row s), num_owned the int32 [B] counts; both updated."""
+        row = page_table_row if page_table_row.ndim == 1 else page_table_row[s]
+        self._i32(row, "page_table_row", 1)
+        self._i32(num_owned, "num_owned", 1)
+        if not 0 <= s < num_owned.shape[0]:
+            raise ValueError("sequence index out of range")
+        cnt = num_owned[s:s + 1]
+        _check(lib().kvarn_page_pool_release(self._h, row.ctypes.data_as(ctypes.c_void_p), row.shape[0],
+                                             cnt.ctypes.data_as(ctypes.c_void_p)), "kvarn_page_pool_release")

@@ -24,6 +24,7 @@ UNITS = [
     ("decode.hip", ["-DKVARN_DECODE_NG=2"], "decode_ng2.o"),
     ("decode.hip", ["-DKVARN_DECODE_NG=4"], "decode_ng4.o"),
     ("prefill.hip", [], "prefill.o"),
+    ("page_pool.cpp", [], "page_pool.o"),
 ]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -258,6 +258,8 @@ const char* kvarn_status_string(kvarn_status s) {
       return "HIP error";
     case KVARN_E_SCRATCH_LIMIT:
       return "needs more workspace than the fixed scratch of the no-allocation entry point";
+    case KVARN_E_OUT_OF_PAGES:
+      return "page pool has too few free pages";
   }
   return "unknown status";
 }

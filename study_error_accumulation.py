@@ -30,7 +30,7 @@ import sys
 import numpy as np
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--prefix", type=int, default=2048, help="prefill tokens (multiple of 128)")
     p.add_argument("--steps", type=int, default=4096, help="decode steps")
@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--feedback", type=float, default=0.02,
                    help="gain of the attention output in the state update (at 0.1 and above the fp16 recurrence "
                         "itself amplifies any perturbation, 8-bit included)")
-    return p.parse_args()
+    p.add_argument("--out", type=str, default="", help="also write the JSON summary to this file")
+    return p.parse_args(argv)
 
 
 def run(args, seed):
@@ -158,6 +159,8 @@ def run(args, seed):
             err_o[("free",) + c].append(o.float() - o_ref.float())
             run.x = advance(run.x, o, i)
         ref.x = advance(ref.x, o_ref.half(), i)
+        if (i + 1) % 512 == 0:
+            print(f"seed {seed}: step {i + 1} of {args.steps}", file=sys.stderr, flush=True)
         for c, run in zip(configs, free):
             err_x[("free",) + c].append(torch.linalg.vector_norm(run.x - ref.x) / torch.linalg.vector_norm(ref.x))
         # keep the reference outputs' norms next to the differences (relative error per step)
@@ -185,10 +188,8 @@ CONFIGS = [("kvarn_k4v2_g128", 8), ("kvarn_k4v2_g128", 0), ("kvarn_k8v8_g128", 8
            ("kvarn_k8v2_g128", 8), ("kvarn_k2v2_g128", 8), ("kvarn_k2v2_g128", 0)]
 
 
-def main():
-    args = parse()
-    seeds = [int(x) for x in args.seeds.split(",")]
-    per_seed = [run(args, sd) for sd in seeds]
+def summarise(args, seeds, per_seed):
+    """One row per (run, format, Sinkhorn iterations): each statistic averaged over the seeds."""
     report = per_seed[0][0]
     rows = []
     for key in per_seed[0][1]:
@@ -200,15 +201,28 @@ def main():
             row["x_rel_l2"] = dict(zip(report, np.mean([r["x"] for r in rs], axis=0).tolist()))
             row["x_rel_l2_steps_after_256"] = float(np.mean([r["x_all"] for r in rs]))
         rows.append(row)
-    print(json.dumps({"study": "error accumulation (synthetic recurrence)", "prefix": args.prefix,
-                      "steps": args.steps, "seeds": seeds, "feedback": args.feedback, "q_heads": 8, "kv_heads": 1,
-                      "window": 64, "statistic": "median over the window (or over steps > 256), mean over seeds",
-                      "rows": rows}), flush=True)
-    for r in rows:
+    return {"study": "error accumulation (synthetic recurrence)", "prefix": args.prefix,
+            "steps": args.steps, "seeds": seeds, "feedback": args.feedback, "q_heads": 8, "kv_heads": 1,
+            "window": 64, "statistic": "median over the window (or over steps > 256), mean over seeds",
+            "rows": rows}
+
+
+def main(argv=None):
+    args = parse(argv)
+    seeds = [int(x) for x in args.seeds.split(",")]
+    per_seed = [run(args, sd) for sd in seeds]
+    summary = summarise(args, seeds, per_seed)
+    print(json.dumps(summary), flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(summary, f, indent=1)
+            f.write("\n")
+    for r in summary["rows"]:
         o = " ".join(f"{v:.3e}" for v in r["o_rel_l2"].values())
         xx = " ".join(f"{v:.3e}" for v in r.get("x_rel_l2", {}).values())
         print(f"{r['run']:6s} {r['format']:16s} it={r['sinkhorn_iters']}  o: {o} | all {r['o_rel_l2_steps_after_256']:.3e}"
               f"   x: {xx} | all {r.get('x_rel_l2_steps_after_256', float('nan')):.3e}", file=sys.stderr)
+    return summary
 
 
 if __name__ == "__main__":
