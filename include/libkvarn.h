@@ -231,8 +231,8 @@ kvarn_status kvarn_page_pool_reserve(kvarn_page_pool* pool, int32_t num_seqs, co
 kvarn_status kvarn_page_pool_release(kvarn_page_pool* pool, int32_t* page_table_row, int32_t max_pages_per_seq,
                                      int32_t* num_owned);
 
-/* Human-readable name of a status. */
-const char* kvarn_status_string(kvarn_status s);
+/* Human-readable name of a status value (any int: values that are no kvarn_status give "unknown status"). */
+const char* kvarn_status_string(int32_t status);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvarn.so")
+# KVARN_LIB selects another build of the same sources (the host-sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("KVARN_LIB") or os.path.join(_HERE, "libkvarn.so")
 
 KVARN_OK, KVARN_E_INVALID_ARG, KVARN_E_UNSUPPORTED, KVARN_E_HIP, KVARN_E_SCRATCH_LIMIT, KVARN_E_OUT_OF_PAGES = range(6)
 

@@ -40,20 +40,32 @@ def _run(cmd, verbose):
         raise RuntimeError("hipcc failed: " + " ".join(cmd[-3:]))
 
 
-def build(verbose: bool = False, extra=()) -> str:
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def build(verbose: bool = False, extra=(), sanitize: bool = False) -> str:
+    """Build libkvarn.so; with sanitize=True, a copy whose host code carries AddressSanitizer and
+    UndefinedBehaviorSanitizer (device code unchanged) into <repo>/_build/libkvarn_san.so, for the CPU
+    tests of the host layer (load it with clang's ASan runtime preloaded)."""
+    lib = os.path.join(ROOT, "_build", "libkvarn_san.so") if sanitize else LIB
+    flags = FLAGS + (SAN_FLAGS if sanitize else [])
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
     with tempfile.TemporaryDirectory(prefix="kvarn_build_") as tmp:
         jobs = []
         for src, defs, obj in UNITS:
-            jobs.append(["hipcc", "-c"] + FLAGS + list(extra) + defs +
+            jobs.append(["hipcc", "-c"] + flags + list(extra) + defs +
                         ["-o", os.path.join(tmp, obj), os.path.join(CSRC, src)])
         workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
         with ThreadPoolExecutor(max_workers=workers) as ex:
             for f in [ex.submit(_run, j, verbose) for j in jobs]:
                 f.result()
-        _run(["hipcc", "-shared", f"--offload-arch={ARCH}", "-o", LIB + ".tmp"] +
-             [os.path.join(tmp, obj) for _, _, obj in UNITS], verbose)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+        link = ["hipcc", "-shared", f"--offload-arch={ARCH}", "-o", lib + ".tmp"]
+        if sanitize:
+            link += ["-shared-libsan", "-fsanitize=address,undefined"]
+        _run(link + [os.path.join(tmp, obj) for _, _, obj in UNITS], verbose)
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 # stand-alone timing programs (not part of the library), built into <repo>/_build/
@@ -73,6 +85,6 @@ def build_probes(verbose: bool = False) -> list:
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv)
     if "--probes" in sys.argv:
         build_probes(verbose="-v" in sys.argv)

@@ -246,8 +246,8 @@ kvarn_status kvarn_prefill_attention(const kvarn_format* f, int32_t num_seqs, in
                                           num_seqs, num_q_heads, num_kv_heads, stream));
 }
 
-const char* kvarn_status_string(kvarn_status s) {
-  switch (s) {
+const char* kvarn_status_string(int32_t status) {
+  switch (status) {
     case KVARN_OK:
       return "ok";
     case KVARN_E_INVALID_ARG:

@@ -10,7 +10,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# KVARN_ORACLE_LIB selects another build of the same source (the sanitizer build of the CPU tests)
+_LIB_PATH = os.environ.get("KVARN_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 T = 128
