@@ -23,7 +23,9 @@ UNITS = [
     ("decode.hip", ["-DKVARN_DECODE_NG=1"], "decode_ng1.o"),
     ("decode.hip", ["-DKVARN_DECODE_NG=2"], "decode_ng2.o"),
     ("decode.hip", ["-DKVARN_DECODE_NG=4"], "decode_ng4.o"),
-    ("prefill.hip", [], "prefill.o"),
+    ("prefill.hip", ["-DKVARN_PREFILL_NG=1"], "prefill_ng1.o"),
+    ("prefill.hip", ["-DKVARN_PREFILL_NG=2"], "prefill_ng2.o"),
+    ("prefill.hip", ["-DKVARN_PREFILL_NG=4"], "prefill_ng4.o"),
     ("page_pool.cpp", [], "page_pool.o"),
 ]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -65,13 +65,25 @@ KVARN_DECL_LAUNCHER(4)
 #undef KVARN_DECL_LAUNCHER
 
 
-// Chunked prefill (one quantisation group per token): grid (num_seqs * num_kv_heads, row blocks of
-// 64 (query token, query head) rows).
+// Chunked prefill: grid (num_seqs * num_kv_heads, row blocks of 64 (query token, query head) rows);
+// ng quantisation groups per token (1, 2, 4).
 bool prefill_supported(int kb, int vb, int ng, int group_size);
 int prefill_row_blocks(int max_q, int group_size);
-hipError_t launch_prefill(int kb, int vb, int group_size, const _Float16* q, const int32_t* q_lens, int max_q,
+hipError_t launch_prefill(int kb, int vb, int ng, int group_size, const _Float16* q, const int32_t* q_lens, int max_q,
                           const uint8_t* cache, int64_t page_stride, const int32_t* page_table, int max_pages,
                           const int32_t* seq_lens, const _Float16* tail_k, const _Float16* tail_v, float sm_scale,
                           _Float16* out, int num_seqs, int num_q_heads, int num_kv_heads, hipStream_t stream);
+// The prefill kernels of one group count, each in its own object.
+#define KVARN_DECL_PF_LAUNCHER(N)                                                                                 \
+  hipError_t launch_prefill_ng##N(int kb, int vb, int group_size, const _Float16* q, const int32_t* q_lens,       \
+                                  int max_q, const uint8_t* cache, int64_t page_stride, const int32_t* page_table, \
+                                  int max_pages, const int32_t* seq_lens, const _Float16* tail_k,                 \
+                                  const _Float16* tail_v, float qscale, float rawscale, _Float16* out,            \
+                                  int num_seqs, int num_kv_heads, int num_q_heads, int row_blocks,                \
+                                  hipStream_t stream);
+KVARN_DECL_PF_LAUNCHER(1)
+KVARN_DECL_PF_LAUNCHER(2)
+KVARN_DECL_PF_LAUNCHER(4)
+#undef KVARN_DECL_PF_LAUNCHER
 
 }  // namespace kvarn

@@ -239,7 +239,8 @@ kvarn_status kvarn_prefill_attention(const kvarn_format* f, int32_t num_seqs, in
   if (page_stride_bytes < R * num_kv_heads || page_stride_bytes % 16 != 0) return KVARN_E_INVALID_ARG;
   if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
   if (kvarn::prefill_row_blocks(max_q, G) > 65535) return KVARN_E_UNSUPPORTED;
-  return hip_status(kvarn::launch_prefill(f->k_bits, f->v_bits, G, static_cast<const _Float16*>(q), q_lens, max_q,
+  return hip_status(kvarn::launch_prefill(f->k_bits, f->v_bits, n_groups(f), G, static_cast<const _Float16*>(q), q_lens,
+                                          max_q,
                                           static_cast<const uint8_t*>(cache), page_stride_bytes, page_table,
                                           max_pages_per_seq, seq_lens, static_cast<const _Float16*>(tail_k),
                                           static_cast<const _Float16*>(tail_v), sm_scale, static_cast<_Float16*>(out),

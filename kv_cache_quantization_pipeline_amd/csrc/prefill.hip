@@ -9,17 +9,27 @@
 //
 // Work split: grid (sequence * kv head, blocks of 64 query rows), a row being a (query token,
 // query head of this kv head) pair, head fastest; 4 waves per workgroup, 16 rows per wave.  The 16
-// MFMA columns of a wave are its 16 query rows.  Per page the wave does what the decode kernel does
-// for one page: QK with the K codes as the A operand and q'' = c_K ⊙ q' (fp16 hi + lo) as the B
-// operand, logits s' (q'' . codes) + m' sigma, the causal mask, an online softmax per row, and PV
-// with the fp16 weights p_t s'_t against the V codes (the zero-point sum as in decode, channel
-// scale c_V on the result).  The fp16 tail is attended in the raw domain: raw q against raw K rows,
-// then the weights against the tail V staged in LDS transposed; that accumulator is added once Hn
-// has been applied to the rotated one.  Only one group per token (g128) is supported here.
+// MFMA columns of a wave are its 16 query rows.
+//
+// Per page, the workgroup converts the page's K and V codes to fp16 once, into LDS, in the MFMA
+// operand layouts (each wave a quarter: token blocks 2w, 2w + 1 of K, channel blocks 2w, 2w + 1 of
+// V), while the page's scale block goes to LDS by asynchronous copy; the next page's codes and
+// scales are already being loaded while the current page is computed.  Each wave then does for its
+// 16 rows what the decode kernel does for one page: QK with the K codes as the A operand and
+// q'' = c_K ⊙ q' (fp16 hi + lo) as the B operand, one accumulator per quantisation group, logits
+// sum_g s'_g (q''_g . codes) + m'_g sigma_g, the causal mask, an online softmax per row, and PV per
+// V group with the fp16 weights p_t s'_t against the V codes (the zero-point sum through one MFMA,
+// channel scale c_V on the result).  The fp16 tail is attended in the raw domain: raw q against raw
+// K rows, then the weights against the tail V staged in LDS transposed; that accumulator is added
+// once Hn has been applied to the rotated one.
 
 #include "kvarn_codes.h"
 #include "kvarn_device.h"
 #include "kvarn_internal.h"
+
+#ifndef KVARN_PREFILL_NG
+#define KVARN_PREFILL_NG 1
+#endif
 
 namespace kvarn {
 
@@ -35,10 +45,56 @@ __device__ __forceinline__ int vt_pos(int t) {
   return (t >> 5) * 32 + ((t >> 2) & 3) * 8 + 2 * (t & 3) + ((t >> 4) & 1);
 }
 
-// lgkmcnt(0): every LDS read of this wave has returned (vmcnt and expcnt not waited for)
-__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// The codes this wave converts for one page: K token blocks 2w, 2w + 1 and V channel blocks 2w, 2w + 1.
+template <int KB, int VB>
+struct PageShare {
+  KRegs<KB> k[2];
+  VRegs<VB> v[2];
+};
 
-template <int KB, int VB, int G>
+template <int KB, int VB>
+__device__ __forceinline__ void load_share(PageShare<KB, VB>& d, __amdgpu_buffer_rsrc_t rs, int wave, int lane) {
+  const uint32_t klo = static_cast<uint32_t>((lane & 15) * 16 * KB + 4 * (lane >> 4) * KB);
+  const uint32_t vlo = static_cast<uint32_t>(lane * 4 * VB);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int koff = (2 * wave + m) * 16 * 16 * KB;
+    if constexpr (KB == 2) {
+      d.k[m].w = bload64(rs, klo, koff);
+    } else if constexpr (KB == 4) {
+      d.k[m].w = bload128(rs, klo, koff);
+    } else {
+      d.k[m].w[0] = bload128(rs, klo, koff);
+      d.k[m].w[1] = bload128(rs, klo, koff + 16);
+    }
+    const int voff = k_code_bytes(KB) + (2 * wave + m) * 64 * 4 * VB;
+    if constexpr (VB == 2) {
+      d.v[m].w = bload64(rs, vlo, voff);
+    } else if constexpr (VB == 4) {
+      d.v[m].w = bload128(rs, vlo, voff);
+    } else {
+      d.v[m].w[0] = bload128(rs, vlo, voff);
+      d.v[m].w[1] = bload128(rs, vlo, voff + 16);
+    }
+  }
+}
+
+// This wave's 1 KB chunks (c = wave, wave + 4, ...) of a page's scale block into the LDS stage.
+template <int KB, int VB, int NG>
+__device__ __forceinline__ void copy_scale_share(float* stage, const uint8_t* rec, int wave, int lane) {
+  constexpr int SC = 2 * half_scale_floats(NG);
+  constexpr int CHUNKS = SC / 256;
+  const uint8_t* sbase = rec + scale_offset(KB, VB);
+  const uint32_t lo = static_cast<uint32_t>(lane * 16);
+#pragma unroll
+  for (int c0 = 0; c0 < CHUNKS; c0 += 4) {
+    const int c = c0 + wave;
+    if (c < CHUNKS)
+      __builtin_amdgcn_global_load_lds(sbase + (lo + static_cast<uint32_t>(c * 1024)), stage + c * 256, 16, 0, 0);
+  }
+}
+
+template <int KB, int VB, int G, int NG>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restrict__ q,
                                                          const int32_t* __restrict__ q_lens, int max_q,
                                                          const uint8_t* __restrict__ cache, int64_t page_stride,
@@ -48,11 +104,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
                                                          const _Float16* __restrict__ tail_v, int num_q_heads,
                                                          int num_kv_heads, float qscale, float rawscale,
                                                          _Float16* __restrict__ out) {
-  constexpr int R = record_bytes(KB, VB, 1);
-  constexpr int SC = 2 * half_scale_floats(1);   // 768 floats of scales per page
-  __shared__ __attribute__((aligned(16))) float qrot[kRowsPerBlock][kCh];
-  __shared__ __attribute__((aligned(16))) float stage[4][SC];
-  __shared__ __attribute__((aligned(16))) _Float16 vt[kCh][kTok];
+  constexpr int R = record_bytes(KB, VB, NG);
+  constexpr int HS = half_scale_floats(NG);  // floats of one half's scales: c, s'[NG], m'[NG]
+  constexpr int SC = 2 * HS;
+  constexpr int EV = 8 / NG;                 // V channel blocks per quantisation group
+  // Scale stages: two (the next page's scales copied while the current page is computed), or one for
+  // four groups per token, whose 9 KB scale block would otherwise leave room for one workgroup per CU.
+  constexpr int NSTAGE = NG == 4 ? 1 : 2;
+  // LDS: the page's codes as fp16 operands (K [mb][kb][lane], V [nb][kb][lane]) and the scale stages.
+  // The query rotation at the start and the tail's transposed V at the end reuse the K region.
+  __shared__ __attribute__((aligned(16))) f16x8 kdq[8][4][64];
+  __shared__ __attribute__((aligned(16))) f16x8 vdq[8][4][64];
+  __shared__ __attribute__((aligned(16))) float stage[NSTAGE][SC];
+  float(*qrot)[kCh] = reinterpret_cast<float(*)[kCh]>(&kdq[0][0][0]);
+  _Float16(*vt)[kTok] = reinterpret_cast<_Float16(*)[kTok]>(&kdq[0][0][0]);
+  static_assert(sizeof(kdq) >= kRowsPerBlock * kCh * sizeof(float), "query rows alias the K codes");
+  static_assert(sizeof(kdq) >= kCh * kTok * sizeof(_Float16), "tail V aliases the K codes");
 
   const int sh = blockIdx.x;
   const int s = sh / num_kv_heads;
@@ -105,10 +172,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
   for (int b = 1; b < 16; b <<= 1) pm = max(pm, __shfl_xor(pm, b));
   const int pmax = __builtin_amdgcn_readfirstlane(pm);  // over the wave's 16 rows
 
+  // a row past the chunk keeps q' = 0 (its logits stay finite; it is never written)
+  const bool col_ok = p_own >= 0;
   float4 qv[8];
 #pragma unroll
-  for (int e8 = 0; e8 < 8; ++e8) qv[e8] = *reinterpret_cast<const float4*>(&qrot[wave * 16 + nl][4 * gr + 16 * e8]);
-  const bool col_ok = p_own >= 0;
+  for (int e8 = 0; e8 < 8; ++e8) {
+    const float4 v = *reinterpret_cast<const float4*>(&qrot[wave * 16 + nl][4 * gr + 16 * e8]);
+    qv[e8] = col_ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // the first key position not visible to every valid row of the wave: pages below it need no mask
+  int pn = col_ok ? p_own : 0x7fffffff;
+#pragma unroll
+  for (int b = 1; b < 16; b <<= 1) pn = min(pn, __shfl_xor(pn, b));
+  const int pmin = __builtin_amdgcn_readfirstlane(pn);
+  __syncthreads();  // the query rows are in registers; the K region is free for the codes
 
   f16x8 ONES;
 #pragma unroll
@@ -143,134 +220,231 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
   };
 
   // ---- quantised pages --------------------------------------------------------------------------
-  const int n_pages = pmax < 0 ? 0 : min(full, (pmax >> 7) + 1);
+  // The page count is the workgroup's (its last row sees the most keys), so that every wave takes
+  // part in converting every page; a wave whose rows see none of a page skips its own arithmetic.
+  int n_pages = 0;
+  {
+    const int i_last = min(n - 1, (row0 + kRowsPerBlock - 1) / G);
+    const int p_last = L - n + i_last;
+    n_pages = min(full, (p_last >> 7) + 1);
+  }
   const int64_t pt_row = static_cast<int64_t>(s) * max_pages;
   const int64_t head_off = static_cast<int64_t>(h) * R;
-  float* const sown = stage[wave];
+  PageShare<KB, VB> share;
+  if (n_pages > 0) {
+    const uint8_t* rec = cache + static_cast<int64_t>(page_table[pt_row]) * page_stride + head_off;
+    load_share<KB, VB>(share, record_rsrc(rec, R), wave, lane);
+    copy_scale_share<KB, VB, NG>(stage[0], rec, wave, lane);
+  }
   for (int p = 0; p < n_pages; ++p) {
-    const int phys = page_table[pt_row + p];
-    const uint8_t* rec[1] = {cache + static_cast<int64_t>(phys) * page_stride + head_off};
-    const __amdgpu_buffer_rsrc_t rs[1] = {record_rsrc(rec[0], R)};
-    KHalf<KB, 1> klo, khi;
-    VAll<VB, 1> vc;
-    load_k_half<KB, 1>(klo, rs, 0, lane);
-    load_k_half<KB, 1>(khi, rs, 1, lane);
-    load_v_all<KB, VB, 1>(vc, rs, lane);
-    lgkm_wait0();  // the previous page's scale reads are done before the stage is overwritten
-    copy_scales<KB, VB, 1, 1>(sown, rec, lane);
+    if constexpr (NSTAGE == 1) {
+      // one stage: page p's scales are copied only now that page p - 1 is done with it
+      if (p > 0)
+        copy_scale_share<KB, VB, NG>(stage[0],
+                                     cache + static_cast<int64_t>(page_table[pt_row + p]) * page_stride + head_off,
+                                     wave, lane);
+    }
+    // this wave's share of page p: codes in registers, scales in the stage
     vmcnt_wait<0>();
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if constexpr (NG == 1)
+          kdq[2 * wave + m][kb][lane] = dequant_k<KB>(share.k[m], kb);
+        else
+          kdq[2 * wave + m][kb][lane] = dequant_k_grouped<KB>(share.k[m], kb);
+        vdq[2 * wave + m][kb][lane] = dequant_v<VB>(share.v[m], kb);
+      }
+    __syncthreads();  // page p complete in LDS
+    if (p + 1 < n_pages) {
+      // page p + 1 in flight while page p is computed; its stage was last read for page p - 1
+      const uint8_t* rec = cache + static_cast<int64_t>(page_table[pt_row + p + 1]) * page_stride + head_off;
+      load_share<KB, VB>(share, record_rsrc(rec, R), wave, lane);
+      if constexpr (NSTAGE == 2) copy_scale_share<KB, VB, NG>(stage[(p + 1) & 1], rec, wave, lane);
+    }
+    const float* const sp = stage[p % NSTAGE];
 
-    // q'' = c_K ⊙ q' of this lane's row as the QK B operand, fp16 hi + lo
-    f16x8 bqh[4], bql[4];
+    if (128 * p <= pmax) {
+      // q'' = c_K ⊙ q' of this lane's row as the QK B operand, fp16 hi + lo
+      f16x8 bqh[4], bql[4];
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
-      const float4 c4 = *reinterpret_cast<const float4*>(sown + 4 * gr + 16 * e8);
-      const float x[4] = {col_ok ? c4.x * qv[e8].x : 0.f, col_ok ? c4.y * qv[e8].y : 0.f,
-                          col_ok ? c4.z * qv[e8].z : 0.f, col_ok ? c4.w * qv[e8].w : 0.f};
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const float4 c4 = *reinterpret_cast<const float4*>(sp + 4 * gr + 16 * e8);
+        const float x[4] = {c4.x * qv[e8].x, c4.y * qv[e8].y, c4.z * qv[e8].z, c4.w * qv[e8].w};
+        if constexpr (NG == 1) {
+          // slot sl of k-step kb holds channel 4 gr + kb + 16 keperm(sl)
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl)
-        if (keperm<KB>(sl) == e8) {
+          for (int sl = 0; sl < 8; ++sl)
+            if (keperm<KB>(sl) == e8) {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const float hi = f16_trunc(x[kb]);
-            bqh[kb][sl] = static_cast<_Float16>(hi);
-            bql[kb][sl] = static_cast<_Float16>(x[kb] - hi);
+              for (int kb = 0; kb < 4; ++kb) {
+                const float hi = f16_trunc(x[kb]);
+                bqh[kb][sl] = static_cast<_Float16>(hi);
+                bql[kb][sl] = static_cast<_Float16>(x[kb] - hi);
+              }
+            }
+        } else {
+          // k-step e8 / 2 holds code e8 of the four units in slots kg_slot(ui, e8 % 2)
+#pragma unroll
+          for (int ui = 0; ui < 4; ++ui) {
+            const float hi = f16_trunc(x[ui]);
+            bqh[e8 >> 1][kg_slot<KB>(ui, e8 & 1)] = static_cast<_Float16>(hi);
+            bql[e8 >> 1][kg_slot<KB>(ui, e8 & 1)] = static_cast<_Float16>(x[ui] - hi);
           }
         }
-    }
-    float sigma;
-    {
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        d = mfma16(ONES, bqh[kb], d);
-        d = mfma16(ONES, bql[kb], d);
       }
-      sigma = d[0];
-    }
+      // sigma_g = sum_j q''_j over quantisation group g (k-steps 4g/NG .. 4(g+1)/NG - 1)
+      float sigma[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 4 * g / NG; kb < 4 * (g + 1) / NG; ++kb) {
+          d = mfma16(ONES, bqh[kb], d);
+          d = mfma16(ONES, bql[kb], d);
+        }
+        sigma[g] = d[0];
+      }
 
-    // QK and the causal mask: key 128 p + 16 mb + 4 gr + i against the row's last position
-    float lg[8][4];
+      // QK and the causal mask: key 128 p + 16 mb + 4 gr + i against the row's last position
+      float lg[8][4];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < 8; ++mb) {
+        f32x4 dg[NG];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f16x8 a = dequant_k<KB>(mb < 4 ? klo.k[0][mb] : khi.k[0][mb - 4], kb);
-        d = mfma16(a, bqh[kb], d);
-        d = mfma16(a, bql[kb], d);
+        for (int g = 0; g < NG; ++g) dg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const f16x8 a = kdq[mb][kb][lane];
+          dg[kb * NG / 4] = mfma16(a, bqh[kb], dg[kb * NG / 4]);
+          dg[kb * NG / 4] = mfma16(a, bql[kb], dg[kb * NG / 4]);
+        }
+        float v4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const float4 sk = *reinterpret_cast<const float4*>(sp + kCh * (1 + g) + 16 * mb + 4 * gr);
+          const float4 mk = *reinterpret_cast<const float4*>(sp + kCh * (1 + NG + g) + 16 * mb + 4 * gr);
+          v4[0] += fmaf(sk.x, dg[g][0], mk.x * sigma[g]);
+          v4[1] += fmaf(sk.y, dg[g][1], mk.y * sigma[g]);
+          v4[2] += fmaf(sk.z, dg[g][2], mk.z * sigma[g]);
+          v4[3] += fmaf(sk.w, dg[g][3], mk.w * sigma[g]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lg[mb][i] = v4[i];
       }
-      const float4 sk = *reinterpret_cast<const float4*>(sown + 128 + 16 * mb + 4 * gr);
-      const float4 mk = *reinterpret_cast<const float4*>(sown + 256 + 16 * mb + 4 * gr);
-      const float skk[4] = {sk.x, sk.y, sk.z, sk.w}, mkk[4] = {mk.x, mk.y, mk.z, mk.w};
+      if (128 * p + 127 > pmin) {
+        // the page reaches past some row's last visible key
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (128 * p + 16 * mb + 4 * gr + i > p_own) lg[mb][i] = -INFINITY;
+      }
+
+      float m_new;
+      bool live;
+      const float alpha = softmax_step(lg, m_new, live);
+
+      // PV weights w_t = p_t s'_t (s' of the token's V group) go to the MFMA in fp16, divided by the
+      // row's largest weight on this page over all groups (W) so that none of the weights that matter
+      // falls into fp16's subnormal range (small token scales of 8-bit values, spread attention); the
+      // row's PV result is multiplied back by W.  (W is bounded below: where every weight on the page
+      // is that small, the page is negligible against the row's running sum, and 1 / W must not
+      // overflow; the weights then round to fp16 zeros.)  With one group, lg keeps w_t after this loop.
+      constexpr float c0 = 0.5f * ((1 << VB) - 1);
+      float psum = 0.f, wmax = 0.f, msum1 = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        float smax[4];
+        if constexpr (NG == 1) {
+          const float4 sv = *reinterpret_cast<const float4*>(sp + HS + kCh + 16 * mb + 4 * gr);
+          const float4 mv = *reinterpret_cast<const float4*>(sp + HS + 2 * kCh + 16 * mb + 4 * gr);
+          smax[0] = sv.x;
+          smax[1] = sv.y;
+          smax[2] = sv.z;
+          smax[3] = sv.w;
+          const float mvv[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = live ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;
+            psum += pr;
+            msum1 = fmaf(pr, mvv[i], msum1);
+            lg[mb][i] = pr * smax[i];  // w_t
+            wmax = fmaxf(wmax, lg[mb][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) smax[i] = 0.f;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const float4 sv = *reinterpret_cast<const float4*>(sp + HS + kCh * (1 + g) + 16 * mb + 4 * gr);
+            smax[0] = fmaxf(smax[0], sv.x);
+            smax[1] = fmaxf(smax[1], sv.y);
+            smax[2] = fmaxf(smax[2], sv.z);
+            smax[3] = fmaxf(smax[3], sv.w);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            lg[mb][i] = live ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;  // p_t
+            psum += lg[mb][i];
+            wmax = fmaxf(wmax, lg[mb][i] * smax[i]);
+          }
+        }
+      }
+      wmax = rows_max4(wmax);
+      const float wscale = fmaxf(wmax, kMinWeightScale);
+      const float inv_ws = 1.0f / wscale;
+      l_part = l_part * alpha + psum;
+      float arow[4], wrow[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = 128 * p + 16 * mb + 4 * gr + i;
-        lg[mb][i] = key <= p_own ? fmaf(skk[i], d[i], mkk[i] * sigma) : -INFINITY;
+        arow[i] = __shfl(alpha, 4 * gr + i);
+        wrow[i] = __shfl(wscale, 4 * gr + i);
+      }
+#pragma unroll
+      for (int gv = 0; gv < NG; ++gv) {
+        f16x8 aw[4];
+        float msum = msum1, wexact = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int mb = 2 * kb + hh;
+            float wv[4];
+            if constexpr (NG == 1) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) wv[r] = lg[mb][r] * inv_ws;
+            } else {
+              const float4 sv = *reinterpret_cast<const float4*>(sp + HS + kCh * (1 + gv) + 16 * mb + 4 * gr);
+              const float4 mv = *reinterpret_cast<const float4*>(sp + HS + kCh * (1 + NG + gv) + 16 * mb + 4 * gr);
+              const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
+              const float mvv[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                msum = fmaf(lg[mb][r], mvv[r], msum);
+                wv[r] = lg[mb][r] * svv[r] * inv_ws;
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              aw[kb][vslot<VB>(hh, r)] = static_cast<_Float16>(wv[r]);
+              wexact += wv[r];
+            }
+          }
+        const f32x4 corr = pv_zero_point<VB>(aw, fmaf(c0, wexact, msum * inv_ws), C0N);
+#pragma unroll
+        for (int nb = EV * gv; nb < EV * gv + EV; ++nb) {
+          f32x4 d = corr;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) d = mfma16(aw[kb], vdq[nb][kb][lane], d);
+          const float cv = sp[HS + 16 * nb + nl];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv * wrow[i] * d[i]);
+        }
       }
     }
-
-    float m_new;
-    bool live;
-    const float alpha = softmax_step(lg, m_new, live);
-
-    // PV weights w_t = p_t s'_t go to the MFMA in fp16, divided by the row's largest weight on this
-    // page (W) so that none of the weights that matter falls into fp16's subnormal range (small
-    // token scales of 8-bit values, spread attention); the row's PV result is multiplied back by W.
-    // The zero-point sum is carried as in decode (codes centred on c0 through one MFMA against -c0).
-    constexpr float c0 = 0.5f * ((1 << VB) - 1);
-    float wv[8][4];
-    float msum = 0.f, psum = 0.f, wmax = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const float4 sv = *reinterpret_cast<const float4*>(sown + 4 * 128 + 16 * mb + 4 * gr);
-      const float4 mv = *reinterpret_cast<const float4*>(sown + 5 * 128 + 16 * mb + 4 * gr);
-      const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
-      const float mvv[4] = {mv.x, mv.y, mv.z, mv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pr = live ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;
-        psum += pr;
-        msum = fmaf(pr, mvv[i], msum);
-        wv[mb][i] = pr * svv[i];
-        wmax = fmaxf(wmax, wv[mb][i]);
-      }
-    }
-    // (bounded below: where every weight on the page is that small, the page is negligible against
-    // the row's running sum, and 1 / wmax must not overflow; the weights then round to fp16 zeros)
-    wmax = rows_max4(wmax);
-    const float wscale = fmaxf(wmax, kMinWeightScale);
-    const float inv_ws = 1.0f / wscale;
-    msum *= inv_ws;
-    f16x8 aw[4];
-    float wexact = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x0 = wv[2 * kb][r] * inv_ws, x1 = wv[2 * kb + 1][r] * inv_ws;
-        aw[kb][vslot<VB>(0, r)] = static_cast<_Float16>(x0);
-        aw[kb][vslot<VB>(1, r)] = static_cast<_Float16>(x1);
-        wexact += x0 + x1;
-      }
-    }
-    l_part = l_part * alpha + psum;
-    const f32x4 corr = pv_zero_point<VB>(aw, fmaf(c0, wexact, msum), C0N);
-    float arow[4], wrow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      arow[i] = __shfl(alpha, 4 * gr + i);
-      wrow[i] = __shfl(wscale, 4 * gr + i);
-    }
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      f32x4 d = corr;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) d = mfma16(aw[kb], dequant_v<VB>(vc.v[0][nb], kb), d);
-      const float cv = sown[3 * 128 + 16 * nb + nl];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[nb][i] = fmaf(acc[nb][i], arow[i], cv * wrow[i] * d[i]);
-    }
+    __syncthreads();  // every wave is done with page p's codes before page p + 1 overwrites them
   }
 
   // ---- the fp16 tail, raw domain ------------------------------------------------------------------
@@ -414,26 +588,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
 
 }  // namespace
 
-bool prefill_supported(int kb, int vb, int ng, int group_size) {
-  return (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8) && ng == 1 &&
-         (group_size == 1 || group_size == 2 || group_size == 4 || group_size == 8 || group_size == 16);
-}
-
-int prefill_row_blocks(int max_q, int group_size) {
-  return static_cast<int>((static_cast<int64_t>(max_q) * group_size + kRowsPerBlock - 1) / kRowsPerBlock);
-}
-
-hipError_t launch_prefill(int kb, int vb, int group_size, const _Float16* q, const int32_t* q_lens, int max_q,
-                          const uint8_t* cache, int64_t page_stride, const int32_t* page_table, int max_pages,
-                          const int32_t* seq_lens, const _Float16* tail_k, const _Float16* tail_v, float sm_scale,
-                          _Float16* out, int num_seqs, int num_q_heads, int num_kv_heads, hipStream_t stream) {
-  if (num_seqs == 0 || max_q == 0) return hipSuccess;
-  const float rawscale = sm_scale * kLog2e;
-  const float qscale = rawscale * 0.08838834764831845f;
-  const dim3 grid(num_seqs * num_kv_heads, prefill_row_blocks(max_q, group_size));
+#define KVARN_PF_NAME2(N) launch_prefill_ng##N
+#define KVARN_PF_NAME(N) KVARN_PF_NAME2(N)
+hipError_t KVARN_PF_NAME(KVARN_PREFILL_NG)(int kb, int vb, int group_size, const _Float16* q, const int32_t* q_lens,
+                                           int max_q, const uint8_t* cache, int64_t page_stride,
+                                           const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                                           const _Float16* tail_k, const _Float16* tail_v, float qscale,
+                                           float rawscale, _Float16* out, int num_seqs, int num_kv_heads,
+                                           int num_q_heads, int row_blocks, hipStream_t stream) {
+  constexpr int NG = KVARN_PREFILL_NG;
+  const dim3 grid(num_seqs * num_kv_heads, row_blocks);
 #define KVARN_PREFILL_CASE(KB_, VB_, G_)                                                                         \
   if (kb == KB_ && vb == VB_ && group_size == G_) {                                                              \
-    hipLaunchKernelGGL((prefill_kernel<KB_, VB_, G_>), grid, dim3(256), 0, stream, q, q_lens, max_q, cache,      \
+    hipLaunchKernelGGL((prefill_kernel<KB_, VB_, G_, NG>), grid, dim3(256), 0, stream, q, q_lens, max_q, cache,  \
                        page_stride, page_table, max_pages, seq_lens, tail_k, tail_v, num_q_heads, num_kv_heads, \
                        qscale, rawscale, out);                                                                   \
     return hipGetLastError();                                                                                    \
@@ -451,5 +618,30 @@ hipError_t launch_prefill(int kb, int vb, int group_size, const _Float16* q, con
 #undef KVARN_PREFILL_CASE
   return hipErrorInvalidValue;
 }
+
+#if KVARN_PREFILL_NG == 1
+bool prefill_supported(int kb, int vb, int ng, int group_size) {
+  return (kb == 2 || kb == 4 || kb == 8) && (vb == 2 || vb == 4 || vb == 8) && (ng == 1 || ng == 2 || ng == 4) &&
+         (group_size == 1 || group_size == 2 || group_size == 4 || group_size == 8 || group_size == 16);
+}
+
+int prefill_row_blocks(int max_q, int group_size) {
+  return static_cast<int>((static_cast<int64_t>(max_q) * group_size + kRowsPerBlock - 1) / kRowsPerBlock);
+}
+
+hipError_t launch_prefill(int kb, int vb, int ng, int group_size, const _Float16* q, const int32_t* q_lens, int max_q,
+                          const uint8_t* cache, int64_t page_stride, const int32_t* page_table, int max_pages,
+                          const int32_t* seq_lens, const _Float16* tail_k, const _Float16* tail_v, float sm_scale,
+                          _Float16* out, int num_seqs, int num_q_heads, int num_kv_heads, hipStream_t stream) {
+  if (num_seqs == 0 || max_q == 0) return hipSuccess;
+  const float rawscale = sm_scale * kLog2e;
+  const float qscale = rawscale * 0.08838834764831845f;
+  auto* fn = ng == 1 ? launch_prefill_ng1 : ng == 2 ? launch_prefill_ng2 : ng == 4 ? launch_prefill_ng4 : nullptr;
+  if (fn == nullptr) return hipErrorInvalidValue;
+  return fn(kb, vb, group_size, q, q_lens, max_q, cache, page_stride, page_table, max_pages, seq_lens, tail_k, tail_v,
+            qscale, rawscale, out, num_seqs, num_kv_heads, num_q_heads, prefill_row_blocks(max_q, group_size),
+            stream);
+}
+#endif
 
 }  // namespace kvarn

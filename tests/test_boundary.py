@@ -165,7 +165,9 @@ def test_prefill_rejects_before_launch():
                                          dummy, dummy, dummy, 0.1, dummy, None)
     assert pre(hq=15) == kv.KVARN_E_INVALID_ARG
     assert pre(hq=12) == kv.KVARN_E_UNSUPPORTED                      # G = 6
-    assert pre(fmt=kv.format_parse("kvarn_k4v2_g64")) == kv.KVARN_E_UNSUPPORTED   # groups: decode only
+    f64 = kv.format_parse("kvarn_k4v2_g64")
+    assert pre(fmt=f64, hq=12) == kv.KVARN_E_UNSUPPORTED                 # grouped formats too: G = 6
+    assert pre(fmt=f64, q=None) == kv.KVARN_E_INVALID_ARG                # grouped formats are supported
     assert pre(q=None) == kv.KVARN_E_INVALID_ARG
     assert pre(stride=R) == kv.KVARN_E_INVALID_ARG
     assert pre(max_q=-1) == kv.KVARN_E_INVALID_ARG

@@ -72,7 +72,7 @@ class Prefill:
         _, o64 = oracle.prefill_attention(self.fmt.k_bits, self.fmt.v_bits, self.q[seqs].view(np.uint16),
                                           self.q_lens[seqs], host, self.stride, self.pt[seqs], self.lens[seqs],
                                           self.tail_k[seqs].view(np.uint16), self.tail_v[seqs].view(np.uint16),
-                                          self.sm, self.hkv)
+                                          self.sm, self.hkv, group=self.fmt.group)
         return o64
 
     def compare(self, gpu, ref, seqs=None):
@@ -98,6 +98,24 @@ QLENS = [40, 128, 5, 0, 300, 64, 127, 1]     # chunk across page + tail, whole p
 def test_prefill_ragged_small(name, G):
     st = Prefill(name, LENS, QLENS, hkv=2, hq=2 * G, seed=31)
     print(f"worst rel L2 {st.compare(st.run_gpu(), st.run_oracle()):.3g}")
+
+
+GROUPED = [f"kvarn_k{kb}v{vb}_g{g}" for g in (64, 32) for kb, vb in ((4, 2), (2, 8), (8, 4), (8, 8))]
+
+
+@pytest.mark.parametrize("name", GROUPED)
+@pytest.mark.parametrize("G", [1, 8, 16])
+def test_prefill_grouped_ragged_small(name, G):
+    """Quantisation groups of 64 and 32 channels: per-group K dot products and scales, per-group V
+    weights and zero points."""
+    st = Prefill(name, LENS, QLENS, hkv=2, hq=2 * G, seed=35)
+    print(f"worst rel L2 {st.compare(st.run_gpu(), st.run_oracle()):.3g}")
+
+
+def test_prefill_grouped_long_context_sampled():
+    lens = [4096 + 130, 4096 + 77]
+    st = Prefill("kvarn_k4v2_g32", lens, [130, 77], hkv=2, hq=16, seed=36)
+    st.compare(st.run_gpu(), st.run_oracle())
 
 
 @pytest.mark.parametrize("G", [2, 4])

@@ -117,7 +117,7 @@ class ScaledCache:
         got = out.cpu().numpy()
         _, ref = oracle.prefill_attention(self.fmt.k_bits, self.fmt.v_bits, q.view(np.uint16), q_lens, self.host,
                                           self.stride, self.pt, self.lens, self.tail_k.view(np.uint16),
-                                          self.tail_v.view(np.uint16), self.sm, self.hkv)
+                                          self.tail_v.view(np.uint16), self.sm, self.hkv, group=self.fmt.group)
         worst = 0.0
         for s in range(self.B):
             for i in range(q_lens[s]):
