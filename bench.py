@@ -87,7 +87,7 @@ def load_traffic(src_hash):
     return t.get("kernels", {})
 
 
-def write_traffic(fetch_csv, write_csv, copy_mib):
+def traffic_from_csv(fetch_csv, write_csv, copy_mib):
     """HBM bytes per launch of the two timed kernels from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
     (KiB per dispatch), each scaled by the factor that maps the same counter of a plain copy of
     copy_mib MiB onto the bytes that copy moves."""
@@ -118,14 +118,23 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
         out["factors"][counter] = factor
         q_grid = Q_TILES * Q_HKV * 256
         quant = [v for name, grid, v in rows if "quantize_tiles_kernel" in name and grid == q_grid]
-        dec = [v for name, grid, v in rows if "decode_kernel" in name]
-        if not quant or not dec:
+        # the step's decode call: the page kernel (grid: B x Hkv workgroups of 256 per split) and the merge
+        # kernel (B x Hq workgroups of 512) of the B 32 x 16K shape
+        per_split = D_B * D_HKV * 256
+        dec = [v for name, grid, v in rows if "decode_kernel" in name and grid % per_split == 0 and grid > per_split]
+        mrg = [v for name, grid, v in rows if "decode_merge_kernel" in name and grid == D_B * D_HQ * 512]
+        if not quant or not dec or not mrg:
             raise SystemExit(f"{path}: missing quantize/decode dispatches")
         per.setdefault("quantize_tiles", 0.0)
         per["quantize_tiles"] += sum(quant) / len(quant) * 1024.0 * factor
         per.setdefault("decode_attention", 0.0)
-        per["decode_attention"] += sum(dec) / len(dec) * 1024.0 * factor
+        per["decode_attention"] += (sum(dec) / len(dec) + sum(mrg) / len(mrg)) * 1024.0 * factor
     out["kernels"] = {k: int(round(v)) for k, v in per.items()}
+    return out
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib):
+    out = traffic_from_csv(fetch_csv, write_csv, copy_mib)
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)

@@ -89,10 +89,12 @@ size_t kvarn_record_bytes(const kvarn_format* f);
 
 /* Workspace bytes kvarn_decode_attention needs for these sizes: the split-K partial results, per
  * (sequence, query head, split) 128 per-channel sums, a running max, a running sum and two pad floats
- * (528 bytes), for the fp16-tail split and for every page split (one page split per 4 groups of
- * pages, a group being 2 pages, or 1 for 16 query heads per kv head, 8-bit codes or groups below 128
- * channels).  The number of splits depends on the page table's width max_pages_per_seq, which is why
- * that and the kv-head count are arguments.  0 for an unsupported format or shape. */
+ * (528 bytes), for the fp16-tail splits and for every page split.  There is one page split per 4 groups
+ * of pages (a group being 2 pages, or 1 for 16 query heads per kv head, 8-bit codes or groups below 128
+ * channels) of the longest possible sequence, and 1 tail split, or 8 (16 tail tokens each) where
+ * num_seqs * num_kv_heads * page splits is below 1024.  The split counts depend on the page table's
+ * width max_pages_per_seq and on the number of (sequence, kv head) pairs, which is why those are
+ * arguments (rather than a maximum context length).  0 for an unsupported format or shape. */
 size_t kvarn_decode_workspace_bytes(const kvarn_format* f, int32_t num_seqs, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t max_pages_per_seq);
 

@@ -70,6 +70,62 @@ def build(verbose: bool = False, extra=(), sanitize: bool = False) -> str:
     return lib
 
 
+def _short_name(mangled: str) -> str:
+    """kernel<template ints> from an Itanium-mangled kernel name of this library."""
+    import re
+    m = re.match(r"_ZN5kvarn(?:12_GLOBAL__N_1)?(\d+)", mangled)
+    if not m:
+        return mangled
+    n = int(m.group(1))
+    name = mangled[m.end():m.end() + n]
+    rest = mangled[m.end() + n:]
+    args = re.match(r"I((?:Li-?\d+E)+)E", rest)
+    return name + ("<" + ", ".join(re.findall(r"Li(-?\d+)E", args.group(1))) + ">" if args else "")
+
+
+def resource_usage(verbose: bool = False) -> str:
+    """Compile every unit with -Rpass-analysis=kernel-resource-usage (objects discarded) and return a
+    markdown table of each kernel's VGPRs, AGPRs, scratch bytes per lane, occupancy and LDS bytes."""
+    import re
+
+    def one(unit, tmp):
+        src, defs, obj = unit
+        cmd = ["hipcc", "-c"] + FLAGS + defs + ["-Rpass-analysis=kernel-resource-usage", "-o",
+                                                os.path.join(tmp, obj), os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stderr)
+            raise RuntimeError("hipcc failed: " + src)
+        out = []
+        for block in re.split(r"remark: [^\n]*Function Name: ", res.stderr)[1:]:
+            def get(key):
+                m = re.search(key + r": (\d+)", block)
+                return int(m.group(1)) if m else -1
+            out.append((block.split()[0], get("VGPRs"), get("AGPRs"), get(r"ScratchSize \[bytes/lane\]"),
+                        get(r"Occupancy \[waves/SIMD\]"), get(r"LDS Size \[bytes/block\]")))
+        return out
+
+    units = [u for u in UNITS if u[0].endswith(".hip")]
+    with tempfile.TemporaryDirectory(prefix="kvarn_ru_") as tmp:
+        workers = max(1, min(len(units), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(lambda u: one(u, tmp), units))
+    seen = {}
+    for rows in results:
+        for r in rows:
+            seen[_short_name(r[0])] = r  # a kernel compiled in several units appears once
+    lines = ["| kernel | VGPRs | AGPRs | scratch B/lane | waves/SIMD | LDS B |", "|---|---:|---:|---:|---:|---:|"]
+    for nm in sorted(seen):
+        r = seen[nm]
+        lines.append(f"| `{nm}` | {r[1]} | {r[2]} | {r[3]} | {r[4]} | {r[5]} |")
+    spill = sum(1 for r in seen.values() if r[3] > 0)
+    lines.append("")
+    lines.append(f"{len(seen)} kernels, {spill} with scratch.")
+    return "\n".join(lines)
+
+
 # stand-alone timing programs (not part of the library), built into <repo>/_build/
 PROBES = [("probes/rotation_probe.hip", "rotation_probe")]
 
@@ -87,6 +143,9 @@ def build_probes(verbose: bool = False) -> list:
 
 
 if __name__ == "__main__":
+    if "--resource-usage" in sys.argv:
+        print(resource_usage(verbose="-v" in sys.argv))
+        sys.exit(0)
     build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv)
     if "--probes" in sys.argv:
         build_probes(verbose="-v" in sys.argv)

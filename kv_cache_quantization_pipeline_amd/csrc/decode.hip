@@ -205,7 +205,8 @@ template <int KB, int VB, int G, int NG>
 __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_kernel(
     const _Float16* __restrict__ q, const uint8_t* __restrict__ cache, int64_t page_stride,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int num_q_heads,
-    int num_kv_heads, float qscale, float* __restrict__ part, int page_splits, const _Float16* __restrict__ tail_k,
+    int num_kv_heads, float qscale, float* __restrict__ part, int tail_splits, int page_splits,
+    const _Float16* __restrict__ tail_k,
     const _Float16* __restrict__ tail_v, float sm_log2e) {
   using Cfg = DecodeCfg<KB, VB, G, NG>;
   constexpr int P = Cfg::P;
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
   const int s = sh / num_kv_heads;
   const int h = sh - s * num_kv_heads;
   const int sp = blockIdx.y;
-  const int n_splits = page_splits + 1;
+  const int n_splits = tail_splits + page_splits;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, gr = lane >> 4;
@@ -231,11 +232,14 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
   // partials of (pair sh, head g): split k at part + ((sh * G + g) * n_splits + k) * kPartFloats
   const int64_t head0 = static_cast<int64_t>(sh) * G;
 
-  if (sp == 0) {
-    // ---- the fp16 tail: raw-domain attention of every head of the pair ------------------------
+  if (sp < tail_splits) {
+    // ---- the fp16 tail: raw-domain attention of every head of the pair, over this tail split's
+    //      share of the tokens (128 / tail_splits consecutive ones) ----------------------------------
     constexpr int HW = (G + 3) / 4;
-    const int nt = len & (kTok - 1);
-    const int64_t tail_off = static_cast<int64_t>(sh) * kTok * kCh;
+    const int share = kTok / tail_splits;
+    const int t0 = sp * share;
+    const int nt = min(max((len & (kTok - 1)) - t0, 0), share);
+    const int64_t tail_off = (static_cast<int64_t>(sh) * kTok + t0) * kCh;
     if (wave < G) {
       float tmt[HW], tlt[HW], traw[HW][2];
       tail_heads<HW, G>(q + (static_cast<int64_t>(s) * num_q_heads + h * G) * kCh, wave, tail_k + tail_off,
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
       for (int hh = 0; hh < HW; ++hh) {
         const int g = wave + 4 * hh;
         if (g < G) {
-          float* po = part + (head0 + g) * n_splits * kPartFloats;
+          float* po = part + ((head0 + g) * n_splits + sp) * kPartFloats;
           *reinterpret_cast<float2*>(po + 2 * lane) = make_float2(traw[hh][0], traw[hh][1]);
           if (lane == 0) *reinterpret_cast<float2*>(po + kSumOff) = make_float2(tmt[hh], tlt[hh]);
         }
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
 
     const int n_pages = len >> 7;
     const int n_groups = (n_pages + P - 1) / P;
-    const int gi = (sp - 1) * 4 + wave;
+    const int gi = (sp - tail_splits) * 4 + wave;
     const bool has_group = gi < n_groups;
 
     float m_col = -INFINITY;   // running max of the column (log2 units), the same in its 4 lanes
@@ -597,13 +601,14 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
   }
 }
 
-// Merge of the split partials of one (sequence, query head) per workgroup of 8 waves: wave w folds
-// page splits 1 + w, 9 + w, ... (rotated domain) with an online rescale, 16 splits' rows in flight at
-// a time, and wave 0 also reads the tail split 0 (raw domain) before its batches.  With M the largest running max and
-// f_k = exp2(M_k - M): L = sum_k f_k L_k, out = (Hn sum_k f_k rot_k + f_0 raw_0) / L; all zero for an
-// empty sequence.  Lane l owns output channels 2l, 2l + 1.
-__global__ __launch_bounds__(512) void decode_merge_kernel(const float* __restrict__ part, int n_splits,
-                                                           _Float16* __restrict__ out) {
+// Merge of the split partials of one (sequence, query head) per workgroup of 8 waves: splits
+// 0 .. tail_splits - 1 are the tail's (raw domain), the rest the pages' (rotated domain).  Wave w folds
+// page splits tail_splits + w, tail_splits + 8 + w, ... with an online rescale, 16 splits' rows in
+// flight at a time, and wave 0 first folds the tail splits the same way.  With M the largest running
+// max and f_k = exp2(M_k - M): L = sum_k f_k L_k, out = (Hn sum_{page k} f_k rot_k + sum_{tail k} f_k
+// raw_k) / L; all zero for an empty sequence.  Lane l owns output channels 2l, 2l + 1.
+__global__ __launch_bounds__(512) void decode_merge_kernel(const float* __restrict__ part, int tail_splits,
+                                                           int n_splits, _Float16* __restrict__ out) {
   constexpr int kBatch = 16, kW = 8;
   __shared__ float2 wacc[kW][64];
   __shared__ float2 wml[kW];
@@ -611,15 +616,37 @@ __global__ __launch_bounds__(512) void decode_merge_kernel(const float* __restri
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float* ph = part + static_cast<int64_t>(hq) * n_splits * kPartFloats;
-  // wave 0 also reads the tail split's partial, before the batches
+  // wave 0 first folds the tail splits (at most kMaxTailSplits) into one raw-domain partial
   float2 tml = make_float2(-INFINITY, 0.f), traw = make_float2(0.f, 0.f);
   if (wave == 0) {
-    tml = *reinterpret_cast<const float2*>(ph + kSumOff);
-    traw = *reinterpret_cast<const float2*>(ph + 2 * lane);
+    float2 ml[kMaxTailSplits], a[kMaxTailSplits];
+#pragma unroll
+    for (int k = 0; k < kMaxTailSplits; ++k) {
+      if (k < tail_splits) {
+        ml[k] = *reinterpret_cast<const float2*>(ph + k * kPartFloats + kSumOff);
+        a[k] = *reinterpret_cast<const float2*>(ph + k * kPartFloats + 2 * lane);
+      } else {
+        ml[k] = make_float2(-INFINITY, 0.f);
+        a[k] = make_float2(0.f, 0.f);
+      }
+    }
+    float Mr = ml[0].x;
+#pragma unroll
+    for (int k = 1; k < kMaxTailSplits; ++k) Mr = fmaxf(Mr, ml[k].x);
+    if (Mr != -INFINITY) {
+      tml = make_float2(Mr, 0.f);
+#pragma unroll
+      for (int k = 0; k < kMaxTailSplits; ++k) {
+        const float f = __builtin_amdgcn_exp2f(ml[k].x - Mr);
+        tml.y = fmaf(ml[k].y, f, tml.y);
+        traw.x = fmaf(a[k].x, f, traw.x);
+        traw.y = fmaf(a[k].y, f, traw.y);
+      }
+    }
   }
 
   float M = -INFINITY, L = 0.f, r0 = 0.f, r1 = 0.f;
-  for (int k0 = 1 + wave; k0 < n_splits; k0 += kW * kBatch) {
+  for (int k0 = tail_splits + wave; k0 < n_splits; k0 += kW * kBatch) {
     float2 ml[kBatch], a[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -701,13 +728,14 @@ static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64
                                   const DecodeWorkspace& ws, int num_seqs, int num_q_heads, int num_kv_heads,
                                   const DecodePlan& plan, hipStream_t stream) {
   const float qscale = sm_scale * kLog2e * 0.08838834764831845f;
-  hipLaunchKernelGGL((decode_kernel<KB, VB, G, NG>), dim3(num_seqs * num_kv_heads, plan.page_splits + 1), dim3(256), 0,
+  hipLaunchKernelGGL((decode_kernel<KB, VB, G, NG>), dim3(num_seqs * num_kv_heads, plan.tail_splits + plan.page_splits),
+                     dim3(256), 0,
                      stream, q, cache, page_stride, page_table, max_pages, seq_lens, num_q_heads, num_kv_heads, qscale,
-                     ws.part, plan.page_splits, tail_k, tail_v, sm_scale * kLog2e);
+                     ws.part, plan.tail_splits, plan.page_splits, tail_k, tail_v, sm_scale * kLog2e);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(num_seqs * num_q_heads), dim3(512), 0, stream, ws.part,
-                     plan.page_splits + 1, out);
+                     plan.tail_splits, plan.tail_splits + plan.page_splits, out);
   return hipGetLastError();
 }
 
@@ -747,19 +775,23 @@ int decode_pages_per_step(int kb, int vb, int ng, int group_size) {
 }
 
 DecodePlan plan_decode(int kb, int vb, int ng, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq) {
-  (void)num_seqs;
-  (void)num_kv_heads;
   DecodePlan p;
   p.pages_per_group = decode_pages_per_step(kb, vb, ng, group_size);
   const int groups_max = (max_pages_per_seq + p.pages_per_group - 1) / p.pages_per_group;
   // one group per wave, 4 waves per page split; at least one page split
   p.page_splits = std::max(1, (groups_max + 3) / 4);
+  // The fp16 tail (up to 127 tokens of every head of a pair) is one split's work, or eight splits' of
+  // one 16-token chunk each where the pages leave the grid with few workgroups: the tail walk is then
+  // on the critical path of the call.
+  const int64_t page_wgs = static_cast<int64_t>(num_seqs) * num_kv_heads * p.page_splits;
+  p.tail_splits = page_wgs < 1024 ? kMaxTailSplits : 1;
   return p;
 }
 
 size_t decode_workspace_bytes(const DecodePlan& plan, int num_seqs, int num_q_heads, int num_kv_heads) {
   (void)num_kv_heads;
-  return static_cast<size_t>(num_seqs) * num_q_heads * (plan.page_splits + 1) * kPartFloats * sizeof(float);
+  return static_cast<size_t>(num_seqs) * num_q_heads * (plan.tail_splits + plan.page_splits) * kPartFloats *
+         sizeof(float);
 }
 
 DecodeWorkspace decode_workspace_layout(void* workspace, const DecodePlan& plan, int num_seqs, int num_q_heads,

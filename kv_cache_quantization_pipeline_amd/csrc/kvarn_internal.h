@@ -16,14 +16,17 @@ hipError_t launch_append(const _Float16* k_new, const _Float16* v_new, int32_t* 
                          int64_t page_stride, int num_seqs, int num_kv_heads, int kb, int vb, int ng, int iters,
                          hipStream_t stream);
 
-// Split-K decode plan: the page kernel's grid is (num_seqs * num_kv_heads, 1 + page_splits)
-// workgroups of 4 waves.  Split 0 of a (sequence, kv head) pair attends over the fp16 tail; split
-// 1 + j streams page groups 4 j .. 4 j + 3 (one group of pages_per_group pages per wave), sized for
+// Split-K decode plan: the page kernel's grid is (num_seqs * num_kv_heads, tail_splits + page_splits)
+// workgroups of 4 waves.  Split i < tail_splits of a (sequence, kv head) pair attends over tail tokens
+// 128 i / tail_splits .. 128 (i + 1) / tail_splits - 1 (1 or kMaxTailSplits splits); split tail_splits + j streams
+// page groups 4 j .. 4 j + 3 (one group of pages_per_group pages per wave), sized for
 // max_pages_per_seq.  A merge kernel of num_seqs * num_q_heads workgroups follows.
 struct DecodePlan {
   int pages_per_group;
+  int tail_splits;
   int page_splits;
 };
+constexpr int kMaxTailSplits = 8;
 // One partial result: 128 per-channel sums, the running max (log2 units), the running sum, 2 pad floats.
 constexpr int kPartFloats = 132;
 
@@ -31,7 +34,7 @@ constexpr int kPartFloats = 132;
 int decode_pages_per_step(int kb, int vb, int ng, int group_size);
 DecodePlan plan_decode(int kb, int vb, int ng, int num_seqs, int num_kv_heads, int group_size, int max_pages_per_seq);
 
-// Decode workspace: the split partials [seq][q head][1 + page_splits][kPartFloats], written by the
+// Decode workspace: the split partials [seq][q head][tail_splits + page_splits][kPartFloats], written by the
 // page kernel and read by the merge kernel of the same call; nothing is kept between calls.
 struct DecodeWorkspace {
   float* part;

@@ -82,7 +82,7 @@ kvarn_status decode_check(const kvarn_format* f, int32_t num_seqs, int32_t num_q
   if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
   const kvarn::DecodePlan plan =
       kvarn::plan_decode(f->k_bits, f->v_bits, n_groups(f), num_seqs, num_kv_heads, G, max_pages_per_seq);
-  if (plan.page_splits + 1 > 65535) return KVARN_E_UNSUPPORTED;
+  if (plan.tail_splits + plan.page_splits > 65535) return KVARN_E_UNSUPPORTED;
   if (static_cast<int64_t>(num_seqs) * num_q_heads > 0x7fffffffLL) return KVARN_E_INVALID_ARG;
   return KVARN_OK;
 }

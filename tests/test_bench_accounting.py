@@ -44,3 +44,35 @@ def test_bench_refuses_more_than_one_gpu():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_traffic_from_pmc_csv_scales_by_the_copy_and_adds_the_merge(tmp_path):
+    """FETCH/WRITE KiB per dispatch -> bytes per launch: each counter scaled so that the plain copy reads
+    the bytes it moves; the decode call is its page kernel plus its merge kernel (B 32 x 16K shape)."""
+    import bench
+    copy_mib = 4
+    q_grid = bench.Q_TILES * bench.Q_HKV * 256
+    d_grid = bench.D_B * bench.D_HKV * 256 * 17
+    m_grid = bench.D_B * bench.D_HQ * 512
+    rows = [("__amd_rocclr_copyBuffer", 1024, 2048.0, 4096.0),       # fetch counts half the copy's bytes
+            ("quantize_tiles_kernel<4,2,1>", q_grid, 1000.0, 300.0),
+            ("quantize_tiles_kernel<4,2,1>", q_grid, 1200.0, 300.0),
+            ("quantize_tiles_kernel<4,2,1>", 4 * q_grid, 9999.0, 9999.0),  # the cache-building launch: ignored
+            ("decode_kernel<4,2,8,1>", d_grid, 500.0, 20.0),
+            ("decode_kernel<4,2,8,1>", 4 * 1 * 256 * 129, 7777.0, 7777.0),  # the long-context shape
+            ("decode_merge_kernel", m_grid, 50.0, 4.0),
+            ("decode_merge_kernel", 32 * 512, 8888.0, 8888.0)]
+    paths = []
+    for name, col in (("FETCH_SIZE", 2), ("WRITE_SIZE", 3)):
+        p = tmp_path / f"{name}.csv"
+        with open(p, "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n")
+            for i, r in enumerate(rows):
+                f.write(f"{i},\"{r[0]}\",{r[1]},{name},{r[col]}\n")
+        paths.append(str(p))
+    out = bench.traffic_from_csv(paths[0], paths[1], copy_mib)
+    ff = copy_mib * (1 << 20) / (2048.0 * 1024)
+    wf = copy_mib * (1 << 20) / (4096.0 * 1024)
+    assert out["factors"] == {"FETCH_SIZE": ff, "WRITE_SIZE": wf}
+    assert out["kernels"]["quantize_tiles"] == round(1100.0 * 1024 * ff + 300.0 * 1024 * wf)
+    assert out["kernels"]["decode_attention"] == round((500.0 + 50.0) * 1024 * ff + (20.0 + 4.0) * 1024 * wf)

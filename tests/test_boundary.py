@@ -64,7 +64,10 @@ def test_record_and_workspace_sizes():
     # 16 page splits of 4 waves plus the tail split; 132 floats per (seq, q head, split)
     assert kv.decode_workspace_bytes(f, 32, 32, 4, 128) == 32 * 32 * (1 + 16) * 132 * 4
     # one page split and the tail split
-    assert kv.decode_workspace_bytes(f, 3, 3, 3, 1) == 3 * 3 * 2 * 132 * 4
+    # few (sequence, kv head) pairs x page splits (under 1024 workgroups): the tail takes 8 splits
+    assert kv.decode_workspace_bytes(f, 3, 3, 3, 1) == 3 * 3 * (8 + 1) * 132 * 4
+    assert kv.decode_workspace_bytes(f, 4, 8, 1, 1025) == 4 * 8 * (8 + 129) * 132 * 4
+    assert kv.decode_workspace_bytes(f, 8, 64, 8, 128) == 8 * 64 * (1 + 16) * 132 * 4
     assert kv.decode_workspace_bytes(f, 32, 24, 4, 128) == 0   # G = 6 unsupported
     for G in (1, 2, 4, 8, 16):
         assert kv.decode_workspace_bytes(f, 4, 2 * G, 2, 16) > 0
