@@ -728,7 +728,7 @@ def main():
         "append_token": {"us": ta * 1e6, "us_median": med[1], "bytes": app_b, "GBps": app_b / ta / 1e9},
         "decode_attention": {"GBps": dec_b / td / 1e9, "frac_hbm": dec_b / td / 1e9 / HBM_PEAK_GBPS,
                              "us": td * 1e6, "us_median": med[2], "bytes": dec_b, "tokens_per_s": D_B / td,
-                             "note": "decode kernel (split-K partials merged by the last workgroup); one layer call, 1 token per sequence"},
+                             "note": "page kernel (split-K partials) + merge kernel; one layer call, 1 token per sequence"},
         "decode_attention_isolated": {
             "us_median": t_iso * 1e6, "bytes": iso_bytes, "GBps": iso_bytes / t_iso / 1e9,
             "frac_hbm": iso_bytes / t_iso / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": D_B / t_iso,
