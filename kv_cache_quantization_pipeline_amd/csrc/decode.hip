@@ -155,7 +155,11 @@ struct DecodeCfg {
   static constexpr int SC = 2 * HS;                 // floats of scales per page
   static constexpr int SO = SC / 256;               // 1 KB LDS copies per page of scales
   // waves per SIMD the register budget is sized for
-  static constexpr int OCC = (KB == 8 || VB == 8 || NG == 4) ? 2 : 3;
+  // (four where the register budget of 128 holds without spilling: 2-bit V, one group, and 2-bit K or
+  // 8 query heads; checked by the build's resource-usage report)
+  static constexpr int OCC = (KB == 8 || VB == 8 || NG == 4)                  ? 2
+                             : (VB == 2 && NG == 1 && (KB == 2 || G == 8)) ? 4
+                                                                          : 3;
 };
 
 template <int KB>
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
     const uint8_t* rec[P];
     __amdgpu_buffer_rsrc_t rs[P];
     float* const stg = buf + wave * (P * SC);
-    PageK<KB> K[P];
+    PageK<KB> K[1];
     if (has_group) {
       const int64_t pt_row = static_cast<int64_t>(s) * max_pages;
       const int64_t head_off = static_cast<int64_t>(h) * R;
@@ -305,8 +309,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
       }
       copy_scales<KB, VB, NG, P>(stg, rec, lane);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int e = 0; e < P; ++e) load_page_k<KB>(K[e], rs[e], lane);
+      load_page_k<KB>(K[0], rs[0], lane);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
     if (has_group) {
       // the scale copy into the stage has landed once only the code loads are outstanding (the
       // compiler does not track the LDS copy itself)
-      vmcnt_wait<P * (KB == 8 ? 16 : 8)>();
+      vmcnt_wait<(KB == 8 ? 16 : 8)>();
 
       const bool valid_own = col_ok && gi * P + e_own < n_pages;
       const float* const sown = stg + e_oc * SC;
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-              const f16x8 a = dequant_k<KB>(K[e].k[mb], kb);
+              const f16x8 a = dequant_k<KB>(K[0].k[mb], kb);
               d = mfma16(a, bqh[kb], d);
               d = mfma16(a, bql[kb], d);
             }
@@ -418,7 +421,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
             for (int g = 0; g < NG; ++g) dg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-              const f16x8 a = dequant_k_grouped<KB>(K[e].k[mb], kb);
+              const f16x8 a = dequant_k_grouped<KB>(K[0].k[mb], kb);
               dg[kb * NG / 4] = mfma16(a, bqh[kb], dg[kb * NG / 4]);
               dg[kb * NG / 4] = mfma16(a, bql[kb], dg[kb * NG / 4]);
             }
@@ -438,6 +441,7 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
           for (int i = 0; i < 4; ++i) lg[mb][i] = (e == 0 || e_own == e) ? v4[i] : lg[mb][i];
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (e + 1 < P) load_page_k<KB>(K[0], rs[e + 1], lane);
         load_page_v<KB, VB>(V[e], rs[e], lane);
         __builtin_amdgcn_sched_barrier(0);
       }
