@@ -265,14 +265,18 @@ def test_prepared_calls_match_plain_calls():
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
-@pytest.mark.parametrize("hkv,extra", [(1, 0), (4, 120)])
-def test_tail_lengths_and_batch_sizes(hkv, extra):
-    """Tail lengths 0, 1, 31, 32, 33, 127 (the tail split reads them in 16-token chunks) and a sequence
-    with no full page, in a small batch on 1 kv head and in a batch of 127 sequences on 4 kv heads.
-    Against the oracle on the GPU's own cache bytes."""
+@pytest.mark.parametrize("name,hkv,extra", [
+    ("kvarn_k4v2_g128", 1, 0),     # few page workgroups: eight tail splits
+    ("kvarn_k4v2_g128", 4, 300),   # 1228 pairs: one tail split
+    ("kvarn_k8v8_g128", 1, 0),     # one page per wave, few page workgroups: eight tail splits
+])
+def test_tail_lengths_and_batch_sizes(name, hkv, extra):
+    """Tail lengths 0, 1, 31, 32, 33, 127 (read in 16-token chunks) and a sequence with no full page, with
+    the tail in eight splits and in one: in a small batch on 1 kv head and in a batch of 307 sequences
+    on 4 kv heads.  Against the oracle on the GPU's own cache bytes."""
     base = [3 * 128, 128 + 1, 2 * 128 + 31, 4 * 128 + 32, 128 + 33, 5 * 128 + 127, 77]
     lens = base + [(i % 9) * 128 + (i * 37) % 128 for i in range(extra)]
-    st = Setup("kvarn_k4v2_g128", lens, hkv=hkv, hq=8 * hkv, seed=36, max_pages=8)
+    st = Setup(name, lens, hkv=hkv, hq=8 * hkv, seed=36, max_pages=8)
     out = st.run_gpu()
     seqs = list(range(len(base)))
     _compare(out[seqs], st.run_oracle(seqs), st.lens[seqs])
