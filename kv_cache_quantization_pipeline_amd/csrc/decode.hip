@@ -605,49 +605,40 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
   }
 }
 
-// Merge of the split partials of one (sequence, query head) per workgroup of 8 waves: splits
-// 0 .. tail_splits - 1 are the tail's (raw domain), the rest the pages' (rotated domain).  Wave w folds
-// page splits tail_splits + w, tail_splits + 8 + w, ... with an online rescale, 16 splits' rows in
-// flight at a time, and wave 0 first folds the tail splits the same way.  With M the largest running
-// max and f_k = exp2(M_k - M): L = sum_k f_k L_k, out = (Hn sum_{page k} f_k rot_k + sum_{tail k} f_k
-// raw_k) / L; all zero for an empty sequence.  Lane l owns output channels 2l, 2l + 1.
-__global__ __launch_bounds__(512) void decode_merge_kernel(const float* __restrict__ part, int tail_splits,
-                                                           int n_splits, _Float16* __restrict__ out) {
-  constexpr int kBatch = 16, kW = 8;
+// Merge of the split partials of one (sequence, query head) per workgroup of W waves (8 waves with 8
+// rows in flight each up to 64 page splits, else 16 with 16): splits 0 .. tail_splits - 1 are the
+// tail's (raw domain), the rest the pages' (rotated domain).  Wave w folds page splits tail_splits + w,
+// tail_splits + W + w, ... with an online rescale, B splits' rows in flight at a time; wave 0 also
+// folds the tail splits, whose rows it loads before its first batch and folds after issuing it, so both
+// are in flight together.  With M the largest running max and f_k = exp2(M_k - M):
+// L = sum_k f_k L_k, out = (Hn sum_{page k} f_k rot_k + sum_{tail k} f_k raw_k) / L; all zero for an
+// empty sequence.  Lane l owns output channels 2l, 2l + 1.
+template <int W, int B>
+__global__ __launch_bounds__(64 * W) void decode_merge_kernel(const float* __restrict__ part, int tail_splits,
+                                                              int n_splits, _Float16* __restrict__ out) {
+  constexpr int kBatch = B, kW = W;
   __shared__ float2 wacc[kW][64];
   __shared__ float2 wml[kW];
   const int hq = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float* ph = part + static_cast<int64_t>(hq) * n_splits * kPartFloats;
-  // wave 0 first folds the tail splits (at most kMaxTailSplits) into one raw-domain partial
-  float2 tml = make_float2(-INFINITY, 0.f), traw = make_float2(0.f, 0.f);
+  // the tail splits' rows (at most kMaxTailSplits), wave 0 only
+  float2 tl_ml[kMaxTailSplits], tl_a[kMaxTailSplits];
   if (wave == 0) {
-    float2 ml[kMaxTailSplits], a[kMaxTailSplits];
 #pragma unroll
     for (int k = 0; k < kMaxTailSplits; ++k) {
       if (k < tail_splits) {
-        ml[k] = *reinterpret_cast<const float2*>(ph + k * kPartFloats + kSumOff);
-        a[k] = *reinterpret_cast<const float2*>(ph + k * kPartFloats + 2 * lane);
+        tl_ml[k] = *reinterpret_cast<const float2*>(ph + k * kPartFloats + kSumOff);
+        tl_a[k] = *reinterpret_cast<const float2*>(ph + k * kPartFloats + 2 * lane);
       } else {
-        ml[k] = make_float2(-INFINITY, 0.f);
-        a[k] = make_float2(0.f, 0.f);
-      }
-    }
-    float Mr = ml[0].x;
-#pragma unroll
-    for (int k = 1; k < kMaxTailSplits; ++k) Mr = fmaxf(Mr, ml[k].x);
-    if (Mr != -INFINITY) {
-      tml = make_float2(Mr, 0.f);
-#pragma unroll
-      for (int k = 0; k < kMaxTailSplits; ++k) {
-        const float f = __builtin_amdgcn_exp2f(ml[k].x - Mr);
-        tml.y = fmaf(ml[k].y, f, tml.y);
-        traw.x = fmaf(a[k].x, f, traw.x);
-        traw.y = fmaf(a[k].y, f, traw.y);
+        tl_ml[k] = make_float2(-INFINITY, 0.f);
+        tl_a[k] = make_float2(0.f, 0.f);
       }
     }
   }
+  bool tail_pending = wave == 0;  // every call has a page split, so wave 0 enters the loop below
+  float2 tml = make_float2(-INFINITY, 0.f), traw = make_float2(0.f, 0.f);
 
   float M = -INFINITY, L = 0.f, r0 = 0.f, r1 = 0.f;
   for (int k0 = tail_splits + wave; k0 < n_splits; k0 += kW * kBatch) {
@@ -661,6 +652,23 @@ __global__ __launch_bounds__(512) void decode_merge_kernel(const float* __restri
       } else {
         ml[u] = make_float2(-INFINITY, 0.f);
         a[u] = make_float2(0.f, 0.f);
+      }
+    }
+    if (tail_pending) {
+      // fold the tail splits into one raw-domain partial
+      tail_pending = false;
+      float Mr = tl_ml[0].x;
+#pragma unroll
+      for (int k = 1; k < kMaxTailSplits; ++k) Mr = fmaxf(Mr, tl_ml[k].x);
+      if (Mr != -INFINITY) {
+        tml = make_float2(Mr, 0.f);
+#pragma unroll
+        for (int k = 0; k < kMaxTailSplits; ++k) {
+          const float f = __builtin_amdgcn_exp2f(tl_ml[k].x - Mr);
+          tml.y = fmaf(tl_ml[k].y, f, tml.y);
+          traw.x = fmaf(tl_a[k].x, f, traw.x);
+          traw.y = fmaf(tl_a[k].y, f, traw.y);
+        }
       }
     }
     float Mb = M;
@@ -738,8 +746,12 @@ static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64
                      ws.part, plan.tail_splits, plan.page_splits, tail_k, tail_v, sm_scale * kLog2e);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_seqs * num_q_heads), dim3(512), 0, stream, ws.part,
-                     plan.tail_splits, plan.tail_splits + plan.page_splits, out);
+  if (plan.page_splits > 8 * 8)
+    hipLaunchKernelGGL((decode_merge_kernel<16, 16>), dim3(num_seqs * num_q_heads), dim3(1024), 0, stream, ws.part,
+                       plan.tail_splits, plan.tail_splits + plan.page_splits, out);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<8, 8>), dim3(num_seqs * num_q_heads), dim3(512), 0, stream, ws.part,
+                       plan.tail_splits, plan.tail_splits + plan.page_splits, out);
   return hipGetLastError();
 }
 
