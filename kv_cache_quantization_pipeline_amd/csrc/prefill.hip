@@ -320,18 +320,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
           dg[kb * NG / 4] = mfma16(a, bqh[kb], dg[kb * NG / 4]);
           dg[kb * NG / 4] = mfma16(a, bql[kb], dg[kb * NG / 4]);
         }
-        float v4[4] = {0.f, 0.f, 0.f, 0.f};
+        // the groups' terms summed from the first one (no 0 + x, which the compiler must keep)
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           const float4 sk = *reinterpret_cast<const float4*>(sp + kCh * (1 + g) + 16 * mb + 4 * gr);
           const float4 mk = *reinterpret_cast<const float4*>(sp + kCh * (1 + NG + g) + 16 * mb + 4 * gr);
-          v4[0] += fmaf(sk.x, dg[g][0], mk.x * sigma[g]);
-          v4[1] += fmaf(sk.y, dg[g][1], mk.y * sigma[g]);
-          v4[2] += fmaf(sk.z, dg[g][2], mk.z * sigma[g]);
-          v4[3] += fmaf(sk.w, dg[g][3], mk.w * sigma[g]);
-        }
+          const float t[4] = {fmaf(sk.x, dg[g][0], mk.x * sigma[g]), fmaf(sk.y, dg[g][1], mk.y * sigma[g]),
+                              fmaf(sk.z, dg[g][2], mk.z * sigma[g]), fmaf(sk.w, dg[g][3], mk.w * sigma[g])};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lg[mb][i] = v4[i];
+          for (int i = 0; i < 4; ++i) lg[mb][i] = g == 0 ? t[i] : lg[mb][i] + t[i];
+        }
       }
       if (128 * p + 127 > pmin) {
         // the page reaches past some row's last visible key
@@ -394,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
       }
       wmax = rows_max4(wmax);
       const float wscale = fmaxf(wmax, kMinWeightScale);
-      const float inv_ws = 1.0f / wscale;
+      const float inv_ws = __builtin_amdgcn_rcpf(wscale);  // within 1 ulp; the result is multiplied by wscale
       l_part = l_part * alpha + psum;
       float arow[4], wrow[4];
 #pragma unroll
@@ -512,7 +510,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
         }
       wmax = rows_max4(wmax);
       const float wscale = fmaxf(wmax, kMinWeightScale);
-      const float inv_ws = 1.0f / wscale;
+      const float inv_ws = __builtin_amdgcn_rcpf(wscale);
       f16x8 aw[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
