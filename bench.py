@@ -14,15 +14,15 @@ alternately, so each kernel's reads come from HBM, not from the 256 MB Infinity 
 
 Prints one JSON line.  value = algorithmic bytes of the step / step time (GB/s); the per-kernel
 numbers (quantize GB/s, decode tokens/s, fractions of the 8 TB/s HBM peak) are in "kernels", with
-the decode also timed on its own (back-to-back calls over rotated cache copies) and the long-context
+the decode also timed on its own (back-to-back calls over rotated cache copies), the long-context
 serving loop (4 sequences x 128K tokens, 8 query / 1 kv head, append + decode per step, five cache
-copies in turn; eager and HIP-graph replay) after the timed steps.
+copies in turn; eager and HIP-graph replay) and the ragged continuous-batching step (64 sequences of
+1K-32K tokens, k4v2 and k8v8 pools, append + decode per step), all after the timed steps.
 
 --variants (a separate run, not the step): the same quantise and decode workloads in the grouped
 formats k4v2 g64 / g32; chunked prefill (4 sequences, a 512-token chunk on top of 16384 cached
-tokens, 32 query / 4 kv heads, k4v2 g128) against the fp16 MFMA peak; and the ragged
-continuous-batching step (64 sequences of 1K-32K tokens, k4v2 and k8v8 pools); one JSON line of its
-own.
+tokens, 32 query / 4 kv heads, k4v2 g128) against the fp16 MFMA peak; and the ragged step again; one
+JSON line of its own.
 """
 import argparse
 import hashlib
@@ -701,6 +701,8 @@ def main():
 
     # the long-context serving loop (4 sequences x 128K tokens, 8 query heads on 1 kv head)
     long_ctx = long_context_steps(kv, synth, dev)
+    # the ragged continuous-batching step (64 sequences of 1K-32K tokens in a k4v2 and a k8v8 pool)
+    ragged = ragged_mixed_steps(kv, synth, dev, args.steps)
 
     # the "achievable" line: a plain device-to-device copy that moves as many bytes (read + write) as
     # one bulk quantise, two copies alternated like the step's inputs (outside the timed step)
@@ -735,6 +737,7 @@ def main():
             "note": ("decode alone: batch 32 x 16384 tokens (no tail), 32 q / 4 kv heads, k4v2; back-to-back calls "
                      "on two cache copies, median of per-call events (page kernel + merge kernel)")},
         "decode_long_context": long_ctx,
+        "decode_step_ragged_mixed": ragged,
         "device_copy": {"us": t_copy * 1e6, "bytes": 2 * n_copy, "GBps": 2 * n_copy / t_copy / 1e9,
                         "frac_hbm": 2 * n_copy / t_copy / 1e9 / HBM_PEAK_GBPS,
                         "note": "plain device copy of the quantise's byte count (read + write): the achievable line"},

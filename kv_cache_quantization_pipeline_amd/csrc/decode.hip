@@ -425,16 +425,15 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
               dg[kb * NG / 4] = mfma16(a, bqh[kb], dg[kb * NG / 4]);
               dg[kb * NG / 4] = mfma16(a, bql[kb], dg[kb * NG / 4]);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v4[i] = 0.f;
+            // the groups' terms summed from the first one (no 0 + x, which the compiler must keep)
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
               const float4 sk = *reinterpret_cast<const float4*>(sown + kCh + kCh * g + 16 * mb + 4 * gr);
               const float4 mk = *reinterpret_cast<const float4*>(sown + kCh * (1 + NG) + kCh * g + 16 * mb + 4 * gr);
-              v4[0] += fmaf(sk.x, dg[g][0], mk.x * sigma[g]);
-              v4[1] += fmaf(sk.y, dg[g][1], mk.y * sigma[g]);
-              v4[2] += fmaf(sk.z, dg[g][2], mk.z * sigma[g]);
-              v4[3] += fmaf(sk.w, dg[g][3], mk.w * sigma[g]);
+              const float t[4] = {fmaf(sk.x, dg[g][0], mk.x * sigma[g]), fmaf(sk.y, dg[g][1], mk.y * sigma[g]),
+                                  fmaf(sk.z, dg[g][2], mk.z * sigma[g]), fmaf(sk.w, dg[g][3], mk.w * sigma[g])};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v4[i] = g == 0 ? t[i] : v4[i] + t[i];
             }
           }
 #pragma unroll
