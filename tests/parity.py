@@ -1,6 +1,6 @@
 """Parity criteria between the HIP path and the oracle (shared by the GPU tests).
 
-Tolerances (fixed before any kernel was written):
+Tolerances (the workload's accuracy targets, set with the first kernels and unchanged since):
   packing / page placement / code layout   bit-exact (codes read from the GPU bytes at the oracle's
                                             positions; exact-code tiles compare whole records)
   channel scales c and token scales s'      relative error <= 1e-5
