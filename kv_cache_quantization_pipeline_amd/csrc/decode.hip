@@ -605,11 +605,11 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
 }
 
 // Merge of the split partials of one (sequence, query head) per workgroup of W waves (8 waves with 8
-// rows in flight each up to 64 page splits, else 16 with 16): splits 0 .. tail_splits - 1 are the
-// tail's (raw domain), the rest the pages' (rotated domain).  Wave w folds page splits tail_splits + w,
-// tail_splits + W + w, ... with an online rescale, B splits' rows in flight at a time; wave 0 also
-// folds the tail splits, whose rows it loads before its first batch and folds after issuing it, so both
-// are in flight together.  With M the largest running max and f_k = exp2(M_k - M):
+// rows in flight each, or 16 with 16 for over 64 page splits and few workgroups): splits 0 ..
+// tail_splits - 1 are the tail's (raw domain), the rest the pages' (rotated domain).  Wave w folds page
+// splits tail_splits + w, tail_splits + W + w, ... with an online rescale, B splits' rows in flight at a
+// time; wave 0 also folds the tail splits, whose rows it loads before its first batch and folds after
+// issuing it, so both are in flight together.  With M the largest running max and f_k = exp2(M_k - M):
 // L = sum_k f_k L_k, out = (Hn sum_{page k} f_k rot_k + sum_{tail k} f_k raw_k) / L; all zero for an
 // empty sequence.  Lane l owns output channels 2l, 2l + 1.
 template <int W, int B>
@@ -745,7 +745,9 @@ static hipError_t launch_decode_t(const _Float16* q, const uint8_t* cache, int64
                      ws.part, plan.tail_splits, plan.page_splits, tail_k, tail_v, sm_scale * kLog2e);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (plan.page_splits > 8 * 8)
+  // 16 waves only where the splits outnumber one 8-wave batch and the (sequence, query head)
+  // workgroups are too few to fill the chip anyway
+  if (plan.page_splits > 8 * 8 && static_cast<int64_t>(num_seqs) * num_q_heads < 512)
     hipLaunchKernelGGL((decode_merge_kernel<16, 16>), dim3(num_seqs * num_q_heads), dim3(1024), 0, stream, ws.part,
                        plan.tail_splits, plan.tail_splits + plan.page_splits, out);
   else
