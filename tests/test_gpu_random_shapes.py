@@ -1,14 +1,20 @@
-"""Seeded random shapes: decode and chunked prefill against the oracle over formats, query heads per kv
-head, kv-head counts, ragged lengths (page boundaries, empty sequences, tails of every size) and page
-tables wider than the lengths need (so the split counts, the tail-split mode and the merge shape vary
-from case to case).  Every case prints its parameters before it runs."""
+"""Seeded random shapes against the oracle: the tile quantiser over formats, iteration counts, tile and
+kv-head counts, magnitudes and token-scale spreads; decode and chunked prefill over formats, query
+heads per kv head, kv-head counts, ragged lengths (page boundaries, empty sequences, tails of every
+size) and page tables wider than the lengths need (so the split counts, the tail-split mode and the
+merge shape vary from case to case).  Every case prints its parameters before it runs."""
 import numpy as np
 import pytest
 
+import oracle
+from parity import assert_code_rate, check_record
 from test_gpu_decode import Setup, _compare
 from test_gpu_prefill import Prefill
 
+torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
+
+import kv_cache_quantization_pipeline_amd as kv  # noqa: E402
 
 FORMATS = [f"kvarn_k{kb}v{vb}_g{g}" for g in (128, 64, 32) for kb in (2, 4, 8) for vb in (2, 4, 8)]
 N_CASES = 60
@@ -56,3 +62,59 @@ def test_random_prefill(i):
     print(f"case {i}: prefill {name} G {G} hkv {hkv} lens {lens} q_lens {q_lens}", flush=True)
     st = Prefill(name, lens, q_lens, hkv=hkv, hq=hkv * G, seed=seed)
     st.compare(st.run_gpu(), st.run_oracle())
+
+
+def _quant_case(i):
+    rng = np.random.default_rng(3000 + i)
+    name = FORMATS[rng.integers(len(FORMATS))]
+    iters = int(rng.choice([8, 8, 8, 1, 3]))
+    T = int(rng.integers(1, 7))
+    hkv = int(rng.integers(1, 6))
+    scale = float(2.0 ** rng.integers(-8, 8))
+    spread = float(rng.choice([0.0, 0.5, 2.3]))       # log-normal token-scale spread (2.3: four decades)
+    return name, iters, T, hkv, scale, spread, rng
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_quantize(i):
+    """Random format, iteration count, tile and kv-head counts, magnitude (x 2^-8 .. 2^7), token-scale
+    spread and outlier channels, with zero tokens and zero channels mixed in; tiles go to permuted
+    pages of a canary-filled pool, and every record must match the oracle's (layout bit-exact,
+    scales and codes to the parity criteria)."""
+    name, iters, T, hkv, scale, spread, rng = _quant_case(i)
+    print(f"case {i}: quantize {name} iters {iters} tiles {T} hkv {hkv} scale {scale} spread {spread}", flush=True)
+    fmt = kv.format_parse(name)
+    fmt.sinkhorn_iters = iters
+    x = rng.standard_normal((2, T, 128, hkv, 128))
+    x *= np.exp(spread * rng.standard_normal((2, T, 128, hkv, 1)))
+    out_ch = rng.integers(0, 128, size=4)
+    x[..., out_ch] *= 20.0
+    x[:, :, rng.integers(0, 128, size=3)] = 0.0          # zero tokens
+    x[..., rng.integers(0, 128, size=2)] = 0.0           # zero channels
+    x = np.clip(x * scale, -60000.0, 60000.0).astype(np.float16)
+    k16, v16 = x[0], x[1]
+    R = kv.record_bytes(fmt)
+    stride = hkv * R
+    n_pool = T + 2
+    pages = rng.permutation(n_pool)[:T].astype(np.int32)
+    cache = torch.full((n_pool * stride,), 0xA5, dtype=torch.uint8, device="cuda")
+    kv.quantize_tiles(fmt, torch.from_numpy(np.ascontiguousarray(k16)).to("cuda"),
+                      torch.from_numpy(np.ascontiguousarray(v16)).to("cuda"), torch.from_numpy(pages).to("cuda"),
+                      cache, stride)
+    torch.cuda.synchronize()
+    host = cache.cpu().numpy()
+    used = np.zeros(n_pool, bool)
+    used[pages] = True
+    for p in np.nonzero(~used)[0]:
+        assert np.all(host[p * stride:(p + 1) * stride] == 0xA5), f"page {p} (not a destination) was written"
+    n_bad = 0
+    for t in range(T):
+        for h in range(hkv):
+            off = int(pages[t]) * stride + h * R
+            rk = oracle.quantize_tile_debug(np.ascontiguousarray(k16[t, :, h]).view(np.uint16), fmt.k_bits, iters,
+                                            group=fmt.group)
+            rv = oracle.quantize_tile_debug(np.ascontiguousarray(v16[t, :, h]).view(np.uint16), fmt.v_bits, iters,
+                                            group=fmt.group)
+            n_bad += check_record(host[off:off + R], fmt.k_bits, fmt.v_bits, rk, rv, f"tile {t} head {h}",
+                                  group=fmt.group)
+    assert_code_rate(n_bad, T * hkv * 2 * 128 * 128, f"case {i}")
