@@ -155,11 +155,11 @@ struct DecodeCfg {
   static constexpr int SC = 2 * HS;                 // floats of scales per page
   static constexpr int SO = SC / 256;               // 1 KB LDS copies per page of scales
   // waves per SIMD the register budget is sized for
-  // (four where the register budget of 128 holds without spilling: 2-bit V, one group, and 2-bit K or
-  // 8 query heads; checked by the build's resource-usage report)
-  static constexpr int OCC = (KB == 8 || VB == 8 || NG == 4)                  ? 2
-                             : (VB == 2 && NG == 1 && (KB == 2 || G == 8)) ? 4
-                                                                          : 3;
+  // (four where the register budget of 128 holds without spilling: 2-bit V, one group, at most 8 query
+  // heads, and 2-bit K or exactly 8 query heads; checked by the build's resource-usage report)
+  static constexpr int OCC = (KB == 8 || VB == 8 || NG == 4)                            ? 2
+                             : (VB == 2 && NG == 1 && G <= 8 && (KB == 2 || G == 8)) ? 4
+                                                                                    : 3;
 };
 
 template <int KB>
