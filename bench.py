@@ -213,6 +213,24 @@ def cpu_baseline(k1, v1, seconds):
             "quantize_GBps": q_bytes / q_time / 1e9, "decode_tokens_per_s": d_calls / d_time}
 
 
+def _blocks_time(fn, per_block, blocks, warmup):
+    """Median over `blocks` blocks of the mean time per call of `per_block` back-to-back calls, each
+    block bracketed by one pair of HIP events on the launch stream (no event between the calls)."""
+    import numpy as np
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(blocks)]
+    for b in range(blocks):
+        ev[b][0].record()
+        for i in range(per_block):
+            fn(warmup + b * per_block + i)
+        ev[b][1].record()
+    torch.cuda.synchronize()
+    return float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3 / per_block
+
+
 def _events_time(fn, steps, warmup):
     import torch
     for i in range(warmup):
@@ -343,9 +361,11 @@ def long_context_steps(kv, synth, dev):
     """4 sequences x 131072 tokens, 8 query heads on 1 kv head, k4v2: 128 steps of append one token +
     decode per copy (the last append of each copy fills the tail and quantises it inline).  The cache
     is 63 MB, so five independent copies (315 MB) are used in turn and every read comes from HBM,
-    not from the 256 MB Infinity Cache.  Timed with HIP events on the launch stream around each call;
-    the calls are prepared (marshalled once), so that the host keeps ahead of the GPU.  Then the same
-    steps are captured as one HIP graph per copy and timed by replay (no host launch cost per call)."""
+    not from the 256 MB Infinity Cache.  The calls are prepared (marshalled once), so that the host keeps
+    ahead of the GPU.  Timed three ways: the eager loop by the host clock with no event between the
+    launches; the same loop with events around every call (the append / decode split); and the steps
+    captured as one HIP graph per copy, timed by replay.  The decode alone is also timed back-to-back
+    over the copies."""
     import numpy as np
     import torch
     w = synth.WORKLOADS["decode_long_b4_ctx128k"]
@@ -401,22 +421,35 @@ def long_context_steps(kv, synth, dev):
                     ev.append(e)
         return ev
 
+    def reset():
+        torch.cuda.synchronize(dev)
+        for c in range(n_copies):
+            lens[c].fill_(ctx)
+            tails[c][0].zero_()
+            tails[c][1].zero_()
+        torch.cuda.synchronize(dev)
+
     run(4, False)                                  # warm-up, then back to the starting state
-    torch.cuda.synchronize(dev)
-    for c in range(n_copies):
-        lens[c].fill_(ctx)
-        tails[c][0].zero_()
-        tails[c][1].zero_()
-    torch.cuda.synchronize(dev)
+    reset()
+    # eager, no events between the launches: the step time by the host clock
     t0 = time.perf_counter()
-    ev = run(n_steps, True)
+    run(n_steps, False)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
     assert lens[0].cpu().tolist() == [ctx + n_steps] * B
-    n = len(ev)
+    n = n_steps * n_copies
+    # the instrumented pass (events around every call): the append / decode split within the loop
+    reset()
+    ev = run(n_steps, True)
+    torch.cuda.synchronize(dev)
     ta = sum(e[0].elapsed_time(e[1]) for e in ev) / n * 1e-3
-    td = sum(e[1].elapsed_time(e[2]) for e in ev) / n * 1e-3
-    td_med = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    td_in = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    # decode alone, back-to-back over the five copies at 64 tail tokens (the loop's mean tail length)
+    for c in range(n_copies):
+        lens[c].fill_(ctx + 64)
+    td_med = _blocks_time(lambda i: decs[i % n_copies](), 4 * n_copies, 5, n_copies)
+    lb64 = np.full(B, ctx + 64, np.int64)
+    b_dec64 = _decode_bytes(lb64, hkv, hq, R)
     b_app = b_dec = 0
     for s in range(n_steps):
         lb = np.full(B, ctx + s, np.int64)
@@ -427,6 +460,7 @@ def long_context_steps(kv, synth, dev):
 
     # the same 128 steps per copy captured once as a HIP graph (append + decode, 256 launches) and
     # replayed, each copy reset to its starting state first; timed with events around each replay
+    reset()
     graphs = []
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(torch.cuda.current_stream(dev))
@@ -440,11 +474,7 @@ def long_context_steps(kv, synth, dev):
         graphs.append(g)
     torch.cuda.current_stream(dev).wait_stream(side)
     ge = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_copies)]
-    for c in range(n_copies):
-        lens[c].fill_(ctx)
-        tails[c][0].zero_()
-        tails[c][1].zero_()
-    torch.cuda.synchronize(dev)
+    reset()
     for c in range(n_copies):
         ge[c][0].record()
         graphs[c].replay()
@@ -459,10 +489,14 @@ def long_context_steps(kv, synth, dev):
             "step_frac_hbm": (b_app + b_dec) / step / 1e9 / HBM_PEAK_GBPS,
             "graph_us_per_step": g_step * 1e6, "graph_tokens_per_s": B / g_step,
             "graph_step_frac_hbm": (b_app + b_dec) / g_step / 1e9 / HBM_PEAK_GBPS,
-            "decode_us": td * 1e6, "decode_us_median": td_med * 1e6, "decode_bytes": b_dec,
-            "decode_GBps": b_dec / td_med / 1e9, "decode_frac_hbm": b_dec / td_med / 1e9 / HBM_PEAK_GBPS,
+            "decode_us": td_med * 1e6, "decode_bytes": b_dec64,
+            "decode_GBps": b_dec64 / td_med / 1e9, "decode_frac_hbm": b_dec64 / td_med / 1e9 / HBM_PEAK_GBPS,
             "decode_tokens_per_s": B / td_med,
-            "append_us": ta * 1e6, "append_bytes": b_app}
+            "decode_note": ("decode alone at 131072 + 64 tokens, back-to-back over the five copies; median over "
+                            "5 blocks of 20 calls of the mean per call"),
+            "instrumented": {"append_us": ta * 1e6, "decode_us_median": td_in * 1e6, "append_bytes": b_app,
+                             "decode_bytes": b_dec,
+                             "note": "the loop again with events around every call (each event adds idle time)"}}
 
 
 def ragged_mixed_steps(kv, synth, dev, steps):
@@ -594,8 +628,9 @@ def main():
     # ---- decode cache: quantise the decode workload's K/V once (untimed), two copies ----------
     w2 = synth.WORKLOADS["decode_gqa8_b32_ctx16k"]
     pages_per_seq = D_CTX // 128
-    # pages for tails that fill during the run: each copy takes (warmup + steps + 1) // 2 appends
-    extra = -(-((args.warmup + args.steps + 1) // 2) // 128) + 1
+    # pages for tails that fill during the run: each copy takes (warmup + 2 steps + 1) // 2 appends
+    # (the timed steps and the instrumented pass after them)
+    extra = -(-((args.warmup + 2 * args.steps + 1) // 2) // 128) + 1
     max_pages = pages_per_seq + extra
     n_pool = D_B * max_pages
     perm2 = synth.gen_page_perm(w2["seed"], n_pool).reshape(D_B, max_pages)
@@ -644,40 +679,56 @@ def main():
         return _append_bytes(lens_before, D_HKV, R)
 
     quant_bytes = Q_TILES * Q_HKV * (2 * 128 * 128 * 2 + R)
-    ev = []
 
-    def step(i, record):
+    # events: None, "quantize" (around the quantise launch only) or "all" (between every launch).
+    # Each event recorded between two launches leaves the GPU idle for a few microseconds, so the timed
+    # steps carry only the two events of the dominant kernel; the append / decode split comes from an
+    # instrumented pass of the same step after them.
+    def step(i, events, ev):
         c = i % 2
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
-        if record:
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4 if events == "all" else 2)] if events else None
+        if events:
             e[0].record()
         kv.quantize_tiles(fmt, k1d[c], v1d[c], pages1, cache1[c], stride1)
-        if record:
+        if events:
             e[1].record()
         kv.append_token(fmt, knew, vnew, lens2[c], tails[c][0], tails[c][1], pt2, cache2[c], stride2)
-        if record:
+        if events == "all":
             e[2].record()
         kv.decode_attention(fmt, q2, cache2[c], stride2, pt2, lens2[c], tails[c][0], tails[c][1], sm, out2, ws2,
                             D_HKV)
-        if record:
+        if events == "all":
             e[3].record()
+        if events:
             ev.append(e)
         b_app = append_bytes(host_lens[c])
         host_lens[c] += 1
         return b_app, decode_bytes(host_lens[c])
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i, None, None)
     torch.cuda.synchronize(dev)
     bytes_app = bytes_dec = 0
+    ev_q = []
     t0 = time.perf_counter()
     for i in range(args.warmup, args.warmup + args.steps):
-        ba, bd = step(i, True)
+        ba, bd = step(i, "quantize", ev_q)
         bytes_app += ba
         bytes_dec += bd
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
     assert torch.isfinite(out2.float()).all().item()
+
+    # the instrumented pass: the same steps with events between all launches (append / decode split)
+    ev = []
+    br_app = br_dec = 0
+    t0 = time.perf_counter()
+    for i in range(args.warmup + args.steps, args.warmup + 2 * args.steps):
+        ba, bd = step(i, "all", ev)
+        br_app += ba
+        br_dec += bd
+    torch.cuda.synchronize(dev)
+    elapsed_br = time.perf_counter() - t0
 
     # isolated decode (the decode workload alone: batch 32 x 16384 tokens, no tail): back-to-back calls
     # on the two cache copies in turn, each bracketed by events on the launch stream; median per call
@@ -685,17 +736,7 @@ def main():
         lens2[c].fill_(D_CTX)
     dec_calls = [kv.prepare_decode_attention(fmt, q2, cache2[c], stride2, pt2, lens2[c], tails[c][0], tails[c][1], sm,
                                              out2, ws2, D_HKV) for c in range(2)]
-    n_iso = 40
-    iso_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_iso)]
-    for i in range(4):
-        dec_calls[i % 2]()
-    torch.cuda.synchronize(dev)
-    for i in range(n_iso):
-        iso_ev[i][0].record()
-        dec_calls[i % 2]()
-        iso_ev[i][1].record()
-    torch.cuda.synchronize(dev)
-    t_iso = float(np.median([e[0].elapsed_time(e[1]) for e in iso_ev])) * 1e-3
+    t_iso = _blocks_time(lambda i: dec_calls[i % 2](), 8, 5, 4)
     iso_bytes = decode_bytes(np.full(D_B, D_CTX, np.int64))
     del dec_calls
 
@@ -712,30 +753,38 @@ def main():
     t_copy = _events_time(lambda i: cdst[i % 2].copy_(csrc[i % 2]), 20, 3)
     del csrc, cdst
 
-    tq = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev) * 1e-3
+    tq = sum(e[0].elapsed_time(e[1]) for e in ev_q) / len(ev_q) * 1e-3
     ta = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev) * 1e-3
     td = sum(e[2].elapsed_time(e[3]) for e in ev) / len(ev) * 1e-3
-    med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in ev])) * 1e3 for i in range(3)]
+    med = [float(np.median([e[0].elapsed_time(e[1]) for e in ev_q])) * 1e3] + \
+          [float(np.median([e[i].elapsed_time(e[i + 1]) for e in ev])) * 1e3 for i in (1, 2)]
     step_s = elapsed / args.steps
     total_bytes = quant_bytes * args.steps + bytes_app + bytes_dec
     value = total_bytes / elapsed / 1e9
-    dec_b = bytes_dec / args.steps
-    app_b = bytes_app / args.steps
+    dec_b = br_dec / args.steps
+    app_b = br_app / args.steps
+    instrumented_step_us = elapsed_br / args.steps * 1e6
 
     src_hash = source_hash()
     traffic = load_traffic(src_hash)
     kernels = {
         "quantize_tiles": {"GBps": quant_bytes / tq / 1e9, "frac_hbm": quant_bytes / tq / 1e9 / HBM_PEAK_GBPS,
                            "us": tq * 1e6, "us_median": med[0], "bytes": quant_bytes, "tile_heads": Q_TILES * Q_HKV},
-        "append_token": {"us": ta * 1e6, "us_median": med[1], "bytes": app_b, "GBps": app_b / ta / 1e9},
+        "append_token": {"us": ta * 1e6, "us_median": med[1], "bytes": app_b, "GBps": app_b / ta / 1e9,
+                         "note": "from the instrumented pass of the step"},
         "decode_attention": {"GBps": dec_b / td / 1e9, "frac_hbm": dec_b / td / 1e9 / HBM_PEAK_GBPS,
                              "us": td * 1e6, "us_median": med[2], "bytes": dec_b, "tokens_per_s": D_B / td,
-                             "note": "page kernel (split-K partials) + merge kernel; one layer call, 1 token per sequence"},
+                             "note": ("page kernel (split-K partials) + merge kernel; one layer call, 1 token per "
+                                      "sequence; from the instrumented pass of the step")},
+        "step_instrumented": {"us_per_step": instrumented_step_us,
+                              "note": ("the same steps with events between all launches, after the timed ones "
+                                       "(the timed steps record events around the quantise only)")},
         "decode_attention_isolated": {
             "us_median": t_iso * 1e6, "bytes": iso_bytes, "GBps": iso_bytes / t_iso / 1e9,
             "frac_hbm": iso_bytes / t_iso / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": D_B / t_iso,
             "note": ("decode alone: batch 32 x 16384 tokens (no tail), 32 q / 4 kv heads, k4v2; back-to-back calls "
-                     "on two cache copies, median of per-call events (page kernel + merge kernel)")},
+                     "on two cache copies (page kernel + merge kernel), median over 5 blocks of 8 calls of the "
+                     "mean per call")},
         "decode_long_context": long_ctx,
         "decode_step_ragged_mixed": ragged,
         "device_copy": {"us": t_copy * 1e6, "bytes": 2 * n_copy, "GBps": 2 * n_copy / t_copy / 1e9,
