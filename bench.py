@@ -143,14 +143,21 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family / model / stepping numbers (a
+    virtualised host may name only the vendor's product line)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block is enough
+                k, _, v = line.partition(":")
+                fields.setdefault(k.strip(), v.strip())
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def cpu_baseline(k1, v1, seconds):

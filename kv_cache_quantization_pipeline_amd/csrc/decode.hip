@@ -492,14 +492,16 @@ __global__ __launch_bounds__(256, (DecodeCfg<KB, VB, G, NG>::OCC)) void decode_k
 #pragma unroll
       for (int sl = 0; sl < 8; ++sl) C0N[sl] = static_cast<_Float16>(-c0);
 
-      // numerators p_t (the lane's tokens of its column)
+      // numerators p_t (the lane's tokens of its column); a column with no live token subtracts +inf,
+      // so that every exponent is -inf and every p_t 0 without a select per token
+      const float m_sub = live ? m_ref : INFINITY;
       float pr[8][4];
       float psum = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[mb][i] = live ? __builtin_amdgcn_exp2f(lg[mb][i] - m_ref) : 0.f;
+          pr[mb][i] = __builtin_amdgcn_exp2f(lg[mb][i] - m_sub);
           psum += pr[mb][i];
         }
       l_lane = psum;

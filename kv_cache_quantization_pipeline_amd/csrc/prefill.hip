@@ -343,6 +343,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
       float m_new;
       bool live;
       const float alpha = softmax_step(lg, m_new, live);
+      // a row with no live key subtracts +inf: every exponent is -inf, every p_t 0, with no select per key
+      const float m_sub = live ? m_new : INFINITY;
 
       // PV weights w_t = p_t s'_t (s' of the token's V group) go to the MFMA in fp16, divided by the
       // row's largest weight on this page over all groups (W) so that none of the weights that matter
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
           const float mvv[4] = {mv.x, mv.y, mv.z, mv.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pr = live ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;
+            const float pr = __builtin_amdgcn_exp2f(lg[mb][i] - m_sub);
             psum += pr;
             msum1 = fmaf(pr, mvv[i], msum1);
             lg[mb][i] = pr * smax[i];  // w_t
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            lg[mb][i] = live ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;  // p_t
+            lg[mb][i] = __builtin_amdgcn_exp2f(lg[mb][i] - m_sub);  // p_t
             psum += lg[mb][i];
             wmax = fmaxf(wmax, lg[mb][i] * smax[i]);
           }
@@ -497,6 +499,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
       float m_new;
       bool live;
       const float alpha = softmax_step(lg, m_new, live);
+      const float m_sub = live ? m_new : INFINITY;
       // weights in fp16 divided by the row's largest (as for the pages), multiplied back after PV
       float pr[8][4];
       float psum = 0.f, wmax = 0.f;
@@ -504,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const _Float16* __restr
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[mb][i] = live ? __builtin_amdgcn_exp2f(lg[mb][i] - m_new) : 0.f;
+          pr[mb][i] = __builtin_amdgcn_exp2f(lg[mb][i] - m_sub);
           psum += pr[mb][i];
           wmax = fmaxf(wmax, pr[mb][i]);
         }
