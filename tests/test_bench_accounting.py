@@ -3,6 +3,7 @@ fraction it reports), against the per-workload figures worked out from the recor
 80,896 B per quantised tile-head (2 x 32 KiB fp16 read, one 15,360 B k4v2 record written),
 15,360 B per cached page-head read by decode, 512 B per fp16 tail token-head (K and V rows)."""
 import numpy as np
+import pytest
 
 import bench
 
@@ -76,3 +77,33 @@ def test_traffic_from_pmc_csv_scales_by_the_copy_and_adds_the_merge(tmp_path):
     assert out["factors"] == {"FETCH_SIZE": ff, "WRITE_SIZE": wf}
     assert out["kernels"]["quantize_tiles"] == round(1100.0 * 1024 * ff + 300.0 * 1024 * wf)
     assert out["kernels"]["decode_attention"] == round((500.0 + 50.0) * 1024 * ff + (20.0 + 4.0) * 1024 * wf)
+
+
+@pytest.mark.gpu
+def test_timing_events_bracket_device_work():
+    """bench.py's fence-free HIP timing events run on torch's own HIP runtime and stream: an interval
+    around a device copy is positive, grows with the work it brackets and stays within the host clock's
+    time for the same work."""
+    import time
+
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    src = torch.ones(64 << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    res = []
+    for n in (1, 8):
+        e0, e1 = bench.TimingEvent(), bench.TimingEvent()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(n):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        ms = e0.elapsed_time(e1)
+        assert 0.0 < ms <= host_ms
+        res.append(ms)
+    assert res[1] > 2 * res[0]
