@@ -669,7 +669,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU; the method needs no cross-GPU exchange "
+        print("bench.py: measures one GPU; the method needs no cross-GPU exchange "
               "(kv heads and sequences shard independently), so runs with --gpus > 1 are not provided.",
               file=sys.stderr)
         sys.exit(2)

@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
   KVARN_OK = 0,
   KVARN_E_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes */
-  KVARN_E_UNSUPPORTED = 2, /* a format, block size, head size or GQA ratio this build does not run */
+  KVARN_E_UNSUPPORTED = 2, /* a format, block size, head size or GQA ratio this library does not run */
   KVARN_E_HIP = 3,         /* a HIP launch or runtime call failed */
   KVARN_E_SCRATCH_LIMIT = 4, /* kvarn_decode_attention_noalloc: the call needs more workspace than its
                                 fixed scratch holds (kvarn_decode_noalloc_max_workspace_bytes) */

@@ -16,8 +16,8 @@
 //           section "Cơ chế hoạt động: Chuẩn hóa phương sai" (4 stages per token tile).
 //   [OPENAIHUB] openai-hub.net/news/593, section "Technical Details" (per-token scale).
 //
-// Where the pages are silent the oracle takes one plain reading; every reading
-// is listed in DESIGN.md ("Readings of the pages").
+// Where the pages are silent the oracle takes one plain reading, stated at the
+// function that applies it.
 //
 // Parity status of each exported function is stated above it.  All of them are
 // pinned by tests/test_oracle_pins.py against closed forms, textbook routines,

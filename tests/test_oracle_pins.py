@@ -194,7 +194,7 @@ def test_record_sizes_and_capacity():
 
 
 def test_pack_golden_bytes_k4v2():
-    # Layout: K unit u of token t holds channels
+    # Layout (the record layout in oracle/kvarn_oracle.cpp): K unit u of token t holds channels
     # u + 16e as nibble e; with q_K[t][j] = j // 16 every unit reads 0x76543210.
     # V unit (nb, gr, nl, half) holds tokens (mb, i) at bits 2(4mb+i): with
     # q_V[t][j] = mb(t) = (t % 64) // 16 the unit's bytes are 00 55 AA FF.
