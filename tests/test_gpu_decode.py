@@ -290,3 +290,13 @@ def test_decode_one_sequence_of_a_million_tokens():
     assert kv.decode_workspace_bytes(st.fmt, 1, 8, 1, st.max_pages) == 8 * (1 + 1025) * 132 * 4
     out = st.run_gpu()
     _compare(out, st.run_oracle(), st.lens)
+
+
+def test_decode_many_short_sequences():
+    """1500 sequences of 0-300 tokens (seeded) on 2 kv heads with 4 query heads each: 3000 page-kernel
+    rows of workgroups and 6000 merge workgroups, most sequences with no full page or one; every
+    (sequence, head) against the oracle."""
+    rng = np.random.default_rng(38)
+    lens = rng.integers(0, 301, size=1500)
+    st = Setup("kvarn_k4v2_g128", lens, hkv=2, hq=8, seed=38)
+    _compare(st.run_gpu(), st.run_oracle(), st.lens)
