@@ -49,8 +49,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100,
-                    help="untimed steps first (the GPU's clocks take ~10 ms of load to settle)")
+    ap.add_argument("--warmup", type=int, default=250,
+                    help="untimed steps first (the step time settles after ~200 steps, ~45 ms of load)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--cpu-seconds", type=float, default=6.0,
                     help="wall seconds per oracle leg (quantise, decode) of the CPU baseline")
@@ -755,9 +755,9 @@ def main():
     quant_bytes = Q_TILES * Q_HKV * (2 * 128 * 128 * 2 + R)
 
     # events: None, "quantize" (around the quantise launch only) or "all" (between every launch).
-    # Each event recorded between two launches leaves the GPU idle for a few microseconds, so the timed
-    # steps carry only the two events of the dominant kernel; the append / decode split comes from an
-    # instrumented pass of the same step after them.
+    # Each event recorded between two launches leaves the GPU idle for a few microseconds, so only every
+    # fifth timed step carries events, the two around the dominant kernel; the append / decode split
+    # comes from an instrumented pass of the same step after the timed ones.
     def step(i, events, ev):
         c = i % 2
         e = [TimingEvent() for _ in range(4 if events == "all" else 2)] if events else None
@@ -786,7 +786,8 @@ def main():
     ev_q = []
     t0 = time.perf_counter()
     for i in range(args.warmup, args.warmup + args.steps):
-        ba, bd = step(i, "quantize", ev_q)
+        # the quantise of every fifth timed step between two events (each event idles the GPU ~4 us)
+        ba, bd = step(i, "quantize" if (i - args.warmup) % 5 == 0 else None, ev_q)
         bytes_app += ba
         bytes_dec += bd
     torch.cuda.synchronize(dev)
